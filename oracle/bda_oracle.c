@@ -1,0 +1,349 @@
+/*
+ * Reference (oracle) for block-diffusion attention and the confidence commit.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, plain CPU definition that
+ * the HIP library is checked against.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load it; the library never does.  It shares
+ * no source, header, table or helper with the HIP path.
+ *
+ * Everything is computed in double precision.  Inputs arrive as float32 arrays
+ * (bf16 and fp32 values are exactly representable there) and are widened to
+ * double before any arithmetic.
+ *
+ * Sources (pages as titled):
+ *  [NLD-3x]  "Analise do acelero de 3x do Nemotron-Labs-Diffusion-8B-Base"
+ *            (doido.pw), sec. 1 "Block Diffusion Attention" (the three mask
+ *            names M_BD, M_OBC, M_BC) and sec. 2 "Linear Speculative Decoding"
+ *            (bidirectional drafting, causal validation, longest matching
+ *            prefix).
+ *  [LLaDA]   "LLaDA2.0-Uni" summary (discuss.pytorch.kr), "Training objective"
+ *            (BDLM: block k of x_t is predicted from the clean blocks x_0,<k
+ *            and its own noisy block x_t,k) and "SPRINT" (confidence c_i is the
+ *            top-1 softmax probability; the accepted set is every position with
+ *            c_n > tau, with at least a per-step quota of acceptances).
+ *  [DGemma]  diffusers "DiffusionGemma" pipeline docs, "Usage"/intro (causal
+ *            encoder fills the KV cache; bidirectional decoder over the canvas
+ *            and that cache) and "Schedulers" (BlockRefinementScheduler commits
+ *            the most confident tokens above a threshold plus a per-step even
+ *            share).
+ *
+ * Readings taken where the pages are silent (each also listed in the design
+ * notes): sequence order [x_t ; x_0]; x_0 queries never see x_t keys; the last
+ * block may be short (block id = floor(position / b)); the query head h uses
+ * kv head floor(h * Hkv / Hq); scale 1/sqrt(d), no bias; decode keys include
+ * the active block as the last n rows; causal is bottom-right aligned
+ * (query i sees keys 0 .. L-n+i); threshold test is strict (c > tau) and taken
+ * in fp32 (the kernel's precision) on the fp64 value rounded to fp32; argmax
+ * ties go to the lowest vocab id, ranking ties to the lowest row index.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_HYBRID = 0, OR_DECODE = 1, OR_CAUSAL = 2 };
+
+/* ---------------------------------------------------------------------- */
+/* Mask                                                                     */
+/* ---------------------------------------------------------------------- */
+
+/* Training form, [NLD-3x] sec. 1 with the BDLM conditioning of [LLaDA]:
+ * positions 0..L-1 are the noisy copy x_t, L..2L-1 the clean copy x_0.
+ *   x_t query, x_t key : same block                 (M_BD, block-diagonal)
+ *   x_t query, x_0 key : key block strictly earlier (M_OBC, offset block-causal)
+ *   x_0 query, x_0 key : key block same or earlier  (M_BC, block-causal)
+ *   x_0 query, x_t key : never                                             */
+static int allowed_hybrid(long i, long j, long L, long b)
+{
+    int qi_noisy = i < L, kj_noisy = j < L;
+    long bq = (qi_noisy ? i : i - L) / b;
+    long bk = (kj_noisy ? j : j - L) / b;
+    if (qi_noisy && kj_noisy) return bq == bk;
+    if (qi_noisy && !kj_noisy) return bk < bq;
+    if (!qi_noisy && !kj_noisy) return bk <= bq;
+    return 0;
+}
+
+/* Decode form ([DGemma] intro; [NLD-3x] sec. 2 drafting): the n active
+ * queries see every one of the L keys (clean prefix + their own block). */
+static int allowed_decode(long i, long j, long L, long n)
+{
+    (void)i; (void)j; (void)L; (void)n;
+    return 1;
+}
+
+/* Verify form ([NLD-3x] sec. 2): causal, with the n queries being the last n
+ * of the L key positions, so query i sees keys 0 .. L-n+i. */
+static int allowed_causal(long i, long j, long L, long n)
+{
+    return j <= L - n + i;
+}
+
+static int allowed(int mode, long i, long j, long L, long n, long b)
+{
+    if (mode == OR_HYBRID) return allowed_hybrid(i, j, L, b);
+    if (mode == OR_DECODE) return allowed_decode(i, j, L, n);
+    return allowed_causal(i, j, L, n);
+}
+
+/* Rows and key count of the dense mask for a mode.  HYBRID: L is the per-half
+ * length, rows = keys = 2L.  DECODE/CAUSAL: L keys, n = block query rows. */
+static void mask_shape(int mode, long L, long block, long* rows, long* keys)
+{
+    if (mode == OR_HYBRID) { *rows = 2 * L; *keys = 2 * L; }
+    else { *rows = block; *keys = L; }
+}
+
+int oracle_mask_shape(int mode, long L, long block, long* rows, long* keys)
+{
+    if (mode < 0 || mode > 2 || L <= 0 || block <= 0) return 1;
+    if (mode == OR_HYBRID && block > L) return 1;
+    if (mode != OR_HYBRID && block > L) return 1;
+    mask_shape(mode, L, block, rows, keys);
+    return 0;
+}
+
+/* Dense mask M[rows][keys] (1 = the query may attend to the key). */
+int oracle_mask(int mode, long L, long block, uint8_t* M)
+{
+    long rows, keys;
+    if (oracle_mask_shape(mode, L, block, &rows, &keys)) return 1;
+    for (long i = 0; i < rows; ++i)
+        for (long j = 0; j < keys; ++j)
+            M[i * keys + j] = (uint8_t)allowed(mode, i, j, L, block, block);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Attention                                                                */
+/* ---------------------------------------------------------------------- */
+
+/* One output row: softmax over the allowed keys of scale * q.k, then the
+ * weighted sum of the allowed value rows.  All in double. */
+static void attend_row(const float* qrow, const float* K, const float* Vv, const uint8_t* Mrow,
+                       long keys, long d, double scale, double* out, double* s)
+{
+    double m = -INFINITY;
+    for (long j = 0; j < keys; ++j) {
+        if (!Mrow[j]) continue;
+        const float* kr = K + j * d;
+        double acc = 0.0;
+        for (long c = 0; c < d; ++c) acc += (double)qrow[c] * (double)kr[c];
+        s[j] = scale * acc;
+        if (s[j] > m) m = s[j];
+    }
+    double Z = 0.0;
+    for (long j = 0; j < keys; ++j) {
+        if (!Mrow[j]) continue;
+        s[j] = exp(s[j] - m);
+        Z += s[j];
+    }
+    for (long c = 0; c < d; ++c) out[c] = 0.0;
+    for (long j = 0; j < keys; ++j) {
+        if (!Mrow[j]) continue;
+        const float* vr = Vv + j * d;
+        double w = s[j] / Z;
+        for (long c = 0; c < d; ++c) out[c] += w * (double)vr[c];
+    }
+}
+
+/*
+ * Attention with an explicit dense mask.
+ *   q   [B, Hq,  rows, d]    k, v [B, Hkv, keys, d]   (float32, row-major)
+ *   out [B, Hq,  rows, d] double, or, when sel != NULL, [nsel, d] for the
+ *       listed (b, h, i) triples in sel[3*t .. 3*t+2].
+ * Returns 0, or 1 on a bad argument.
+ */
+int oracle_attention(int mode, const float* q, const float* k, const float* v, double* out,
+                     long B, long Hq, long Hkv, long L, long d, long block,
+                     const long* sel, long nsel, int nthreads)
+{
+    long rows, keys;
+    if (oracle_mask_shape(mode, L, block, &rows, &keys)) return 1;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv) return 1;
+    uint8_t* M = (uint8_t*)malloc((size_t)rows * (size_t)keys);
+    if (!M) return 1;
+    oracle_mask(mode, L, block, M);
+    double scale = 1.0 / sqrt((double)d);
+    long group = Hq / Hkv;
+    long total = sel ? nsel : B * Hq * rows;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int fail = 0;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)keys);
+        if (!s) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (long t = 0; t < total; ++t) {
+                long b, h, i;
+                if (sel) { b = sel[3 * t]; h = sel[3 * t + 1]; i = sel[3 * t + 2]; }
+                else { b = t / (Hq * rows); h = (t / rows) % Hq; i = t % rows; }
+                long g = h / group;
+                const float* qrow = q + ((b * Hq + h) * rows + i) * d;
+                const float* K = k + (b * Hkv + g) * keys * d;
+                const float* Vv = v + (b * Hkv + g) * keys * d;
+                attend_row(qrow, K, Vv, M + i * keys, keys, d, scale, out + t * d, s);
+            }
+            free(s);
+        }
+    }
+    free(M);
+    return fail;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Confidence commit ([LLaDA] SPRINT; [DGemma] Schedulers)                  */
+/* ---------------------------------------------------------------------- */
+
+/* Row statistics on the stored values: the largest logit m, its lowest index
+ * a, and Z = sum_v exp(l_v - m), so the top-1 softmax probability is 1/Z. */
+static void row_stats(const float* row, long V, double* m_out, long* a_out, double* Z_out)
+{
+    double m = (double)row[0];
+    long a = 0;
+    for (long j = 1; j < V; ++j)
+        if ((double)row[j] > m) { m = (double)row[j]; a = j; }
+    double Z = 0.0;
+    for (long j = 0; j < V; ++j) Z += exp((double)row[j] - m);
+    *m_out = m; *a_out = a; *Z_out = Z;
+}
+
+/*
+ * Commit on logits [G, R, V] (float32 holding bf16/fp32 values).
+ * For every group g, among rows r with masked[g,r] = 1:
+ *   p_r  = top-1 softmax probability (double), decided on (float)p_r;
+ *   C    = { r : (float)p_r > threshold }  (strict, fp32);
+ *   need = min(k_min, #masked) - |C|; if need > 0, the `need` masked rows not
+ *          in C with the largest (float)p_r join C (ties: lower row first);
+ *   for r in C: tokens[g,r] = argmax_r, masked[g,r] = 0.  Other rows untouched.
+ * Diagnostics (may be NULL): p64[G*R] (NaN for rows not masked on entry),
+ * argmax[G*R] (-1 likewise), margin[G*R] = |p64 - threshold| (NaN likewise),
+ * gap[G] = (float)p of the last row taken by the fallback minus that of the
+ * first masked row left out (INFINITY when no fallback choice was made).
+ */
+int oracle_commit(const float* logits, int64_t* tokens, uint8_t* masked, float threshold, long k_min,
+                  long G, long R, long V, double* p64, int64_t* argmax, double* margin, double* gap,
+                  int nthreads)
+{
+    if (G < 0 || R < 0 || V <= 0 || k_min < 0) return 1;
+    if (isnan(threshold)) return 1;
+    double* p = (double*)malloc(sizeof(double) * (size_t)(G * R + 1));
+    long* a = (long*)malloc(sizeof(long) * (size_t)(G * R + 1));
+    if (!p || !a) { free(p); free(a); return 1; }
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long t = 0; t < G * R; ++t) {
+        p[t] = NAN; a[t] = -1;
+        if (!masked[t]) continue;
+        double m, Z;
+        long idx;
+        row_stats(logits + t * V, V, &m, &idx, &Z);
+        p[t] = 1.0 / Z;
+        a[t] = idx;
+    }
+    double tau64 = (double)threshold;
+    for (long g = 0; g < G; ++g) {
+        const long base = g * R;
+        long nmasked = 0;
+        for (long r = 0; r < R; ++r) nmasked += masked[base + r] != 0;
+        uint8_t* take = (uint8_t*)calloc((size_t)R + 1, 1);
+        if (!take) { free(p); free(a); return 1; }
+        long ntake = 0;
+        for (long r = 0; r < R; ++r)
+            if (masked[base + r] && (float)p[base + r] > threshold) { take[r] = 1; ++ntake; }
+        long quota = k_min < nmasked ? k_min : nmasked;
+        long need = quota - ntake;
+        float last_in = NAN;
+        for (long step = 0; step < need; ++step) {
+            long best = -1;
+            for (long r = 0; r < R; ++r) {
+                if (!masked[base + r] || take[r]) continue;
+                if (best < 0 || (float)p[base + r] > (float)p[base + best]) best = r;
+            }
+            take[best] = 1; ++ntake;
+            last_in = (float)p[base + best];
+        }
+        if (gap) {
+            gap[g] = INFINITY;
+            if (need > 0) {
+                long first_out = -1;
+                for (long r = 0; r < R; ++r) {
+                    if (!masked[base + r] || take[r]) continue;
+                    if (first_out < 0 || (float)p[base + r] > (float)p[base + first_out]) first_out = r;
+                }
+                if (first_out >= 0) gap[g] = (double)last_in - (double)(float)p[base + first_out];
+            }
+        }
+        for (long r = 0; r < R; ++r) {
+            long t = base + r;
+            if (p64) p64[t] = p[t];
+            if (argmax) argmax[t] = a[t];
+            if (margin) margin[t] = masked[t] ? fabs(p[t] - tau64) : NAN;
+        }
+        for (long r = 0; r < R; ++r) {
+            if (!take[r]) continue;
+            tokens[base + r] = a[base + r];
+            masked[base + r] = 0;
+        }
+        free(take);
+    }
+    free(p);
+    free(a);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Verify ([NLD-3x] sec. 2)                                                 */
+/* ---------------------------------------------------------------------- */
+
+/* argmax_out[b,j] = lowest index of the largest logit of row (b, j);
+ * accept[b] = first j with argmax != drafts[b,j], or R when all agree. */
+int oracle_verify(const float* logits, const int64_t* drafts, int64_t* argmax_out, int32_t* accept,
+                  long B, long R, long V, int nthreads)
+{
+    if (B < 0 || R < 0 || V <= 0) return 1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long t = 0; t < B * R; ++t) {
+        const float* row = logits + t * V;
+        double m = (double)row[0];
+        long idx = 0;
+        for (long j = 1; j < V; ++j)
+            if ((double)row[j] > m) { m = (double)row[j]; idx = j; }
+        argmax_out[t] = idx;
+    }
+    for (long b = 0; b < B; ++b) {
+        long acc = R;
+        for (long j = 0; j < R; ++j)
+            if (argmax_out[b * R + j] != drafts[b * R + j]) { acc = j; break; }
+        accept[b] = (int32_t)acc;
+    }
+    return 0;
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

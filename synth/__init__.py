@@ -1,0 +1,213 @@
+"""Seeded synthetic inputs for block-diffusion attention and the confidence commit.
+
+This module only draws random numbers and lays them out.  It holds none of the
+method's arithmetic (no mask, no softmax, no argmax search): both the HIP path
+and the CPU oracle consume the bytes it returns, and neither imports the other.
+
+All draws use ``torch.Generator().manual_seed(seed)`` on the CPU, in the order
+written below.  Floating values are drawn as fp32 ``randn() * sigma`` (sigma is
+a standard deviation) and cast to bfloat16 with round-to-nearest-even where the
+workload is bf16.
+
+Workload shapes follow the pages' parameters: block 28 and threshold 0.85
+(Nemotron-Labs-Diffusion-VLM-8B usage page, "basic usage"), canvas 256 and 48
+steps with threshold 0.9 (diffusers DiffusionGemma page, "Usage" and
+"Schedulers"), a 1540x1540 image cut into 14x14 patches with a 2x2 merge
+(VLM-8B page, "high-resolution image support").
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import torch
+
+VOCAB = 131072
+
+
+def _gen(seed: int) -> torch.Generator:
+    g = torch.Generator()
+    g.manual_seed(int(seed))
+    return g
+
+
+def normal(shape, sigma: float, g: torch.Generator, dtype=torch.bfloat16) -> torch.Tensor:
+    """fp32 N(0, sigma^2) draw, cast to ``dtype`` (RNE for bf16)."""
+    x = torch.randn(*shape, generator=g, dtype=torch.float32)
+    if sigma != 1.0:
+        x = x * sigma
+    return x.to(dtype)
+
+
+def planted_logits(G: int, R: int, V: int, sigma: float, g: torch.Generator,
+                   dtype=torch.bfloat16, lo: float = 2.0, hi: float = 12.0):
+    """Noise logits with one planted peak per row.
+
+    Each row is N(0, sigma^2) noise (cast to ``dtype``); a uniformly drawn
+    index is then overwritten with (largest noise value of that row) + U(lo, hi),
+    cast to ``dtype``.  The planted index is returned: it is the row's unique
+    largest entry by construction (the gap is at least ``lo`` before rounding).
+    Draw order: noise, planted indices, offsets.
+    """
+    noise = normal((G, R, V), sigma, g, dtype)
+    idx = torch.randint(0, V, (G, R), generator=g, dtype=torch.int64)
+    off = lo + (hi - lo) * torch.rand(G, R, generator=g, dtype=torch.float32)
+    top = noise.float().amax(dim=-1)
+    peak = (top + off).to(dtype)
+    noise.scatter_(-1, idx.unsqueeze(-1), peak.unsqueeze(-1))
+    return noise, idx
+
+
+def redraw_rows(logits: torch.Tensor, idx: torch.Tensor, rows, seed: int, sigma: float,
+                lo: float = 2.0, hi: float = 12.0):
+    """Deterministically redraw the listed (g, r) rows in place.
+
+    Used to keep threshold decisions away from the guard band: the caller
+    decides which rows to redraw; this function only draws new noise and a new
+    plant for them from ``seed``, in the listed order.
+    """
+    g = _gen(seed)
+    V = logits.shape[-1]
+    for (gi, ri) in rows:
+        row = normal((V,), sigma, g, logits.dtype)
+        j = int(torch.randint(0, V, (1,), generator=g).item())
+        off = lo + (hi - lo) * torch.rand(1, generator=g).item()
+        row[j] = (row.float().max() + off).to(logits.dtype)
+        logits[gi, ri] = row
+        idx[gi, ri] = j
+    return logits, idx
+
+
+# --------------------------------------------------------------------------
+# Workloads (shapes and seeds).  "L" below is the per-half length in the
+# training form and the total KV length in the decode/verify forms.
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class AttnCase:
+    mode: str            # "hybrid" | "decode" | "causal"
+    q: torch.Tensor      # [B, Hq, Sq, d]
+    k: torch.Tensor      # [B, Hkv, Sk, d]
+    v: torch.Tensor      # [B, Hkv, Sk, d]
+    L: int
+    block: int
+
+
+def tiny(seed_qkv: int = 0, seed_mask: int = 1):
+    """Tiny case: B=1, L=64 per half, block 4, Hq=Hkv=2, d=32, fp32 N(0,1)
+    Q/K/V; then fp32 logits [1,64,1000] with sigma 2 from the same stream;
+    masked [1,64] ~ Bernoulli(0.5) from ``seed_mask``."""
+    g = _gen(seed_qkv)
+    q = normal((1, 2, 128, 32), 1.0, g, torch.float32)
+    k = normal((1, 2, 128, 32), 1.0, g, torch.float32)
+    v = normal((1, 2, 128, 32), 1.0, g, torch.float32)
+    logits = normal((1, 64, 1000), 2.0, g, torch.float32)
+    gm = _gen(seed_mask)
+    masked = (torch.rand(1, 64, generator=gm) < 0.5).to(torch.uint8)
+    return AttnCase("hybrid", q, k, v, L=64, block=4), logits, masked
+
+
+def hybrid_train(seed: int = 2, B: int = 4, L: int = 2048, block: int = 32,
+                 Hq: int = 32, Hkv: int = 8, d: int = 128) -> AttnCase:
+    """Training form over [x_t ; x_0]: Q [B,Hq,2L,d], K/V [B,Hkv,2L,d] bf16 N(0,1)."""
+    g = _gen(seed)
+    q = normal((B, Hq, 2 * L, d), 1.0, g)
+    k = normal((B, Hkv, 2 * L, d), 1.0, g)
+    v = normal((B, Hkv, 2 * L, d), 1.0, g)
+    return AttnCase("hybrid", q, k, v, L=L, block=block)
+
+
+def decode_block(seed: int = 3, B: int = 32, prefix: int = 4096, n: int = 28,
+                 Hq: int = 32, Hkv: int = 8, d: int = 128) -> AttnCase:
+    """Decode form: an active block of n queries over prefix + own block keys."""
+    g = _gen(seed)
+    q = normal((B, Hq, n, d), 1.0, g)
+    k = normal((B, Hkv, prefix + n, d), 1.0, g)
+    v = normal((B, Hkv, prefix + n, d), 1.0, g)
+    return AttnCase("decode", q, k, v, L=prefix + n, block=n)
+
+
+def verify_block(seed: int = 5, B: int = 16, cache: int = 8192, n: int = 28,
+                 Hq: int = 32, Hkv: int = 8, d: int = 128) -> AttnCase:
+    """Verify form: n drafted queries, causal over cache + drafts (bottom-right)."""
+    g = _gen(seed)
+    q = normal((B, Hq, n, d), 1.0, g)
+    k = normal((B, Hkv, cache + n, d), 1.0, g)
+    v = normal((B, Hkv, cache + n, d), 1.0, g)
+    return AttnCase("causal", q, k, v, L=cache + n, block=n)
+
+
+def commit_logits(seed: int = 4, G: int = 32, R: int = 28, V: int = VOCAB, sigma: float = 3.0):
+    """bf16 logits [G,R,V] with planted peaks; every position still masked."""
+    g = _gen(seed)
+    logits, idx = planted_logits(G, R, V, sigma, g)
+    masked = torch.ones(G, R, dtype=torch.uint8)
+    return logits, idx, masked
+
+
+def verify_drafts(planted_idx: torch.Tensor, seed: int = 7, p: float = 0.2, V: int = VOCAB):
+    """Drafts that agree with the planted peaks for a geometric-length prefix.
+
+    accept_b ~ Geometric(p) - 1 (number of failures before the first success),
+    capped at R.  drafts[b, j] = planted[b, j] for j < accept_b; at j = accept_b
+    the draft is (planted + 1 + r) mod V with r ~ U[0, V-1) so it differs; later
+    positions are uniform ids.  Returns (drafts int64 [B,R], planted accept [B]).
+    """
+    B, R = planted_idx.shape
+    g = _gen(seed)
+    u = torch.rand(B, generator=g, dtype=torch.float64)
+    acc = torch.floor(torch.log1p(-u) / math.log1p(-p)).to(torch.int64).clamp(max=R)
+    r = torch.randint(0, V - 1, (B,), generator=g, dtype=torch.int64)
+    rest = torch.randint(0, V, (B, R), generator=g, dtype=torch.int64)
+    drafts = rest.clone()
+    for b in range(B):
+        a = int(acc[b])
+        drafts[b, :a] = planted_idx[b, :a]
+        if a < R:
+            drafts[b, a] = (planted_idx[b, a] + 1 + r[b]) % V
+    return drafts, acc
+
+
+# --------------------------------------------------------------------------
+# Long multimodal prefill + canvas
+# --------------------------------------------------------------------------
+
+IMAGE_SIDE = 1540
+PATCH = 14
+MERGE = 2
+GRID = IMAGE_SIDE // PATCH // MERGE          # 55 merged tokens per image row
+IMAGE_TOKENS = GRID * GRID                   # 3025
+ROW_BREAKS = GRID                            # one break token per image row
+TEXT_TOKENS = 1016
+PREFIX = IMAGE_TOKENS + ROW_BREAKS + TEXT_TOKENS   # 4096
+CANVAS = 256
+CANVAS_BLOCK = 28
+
+
+def canvas_blocks(canvas: int = CANVAS, block: int = CANVAS_BLOCK):
+    """Block lengths of the canvas: full blocks, then a short last block."""
+    out = [block] * (canvas // block)
+    if canvas % block:
+        out.append(canvas % block)
+    return out
+
+
+def multimodal_prefill(seed: int = 8, B: int = 2, Hq: int = 32, Hkv: int = 8, d: int = 128) -> AttnCase:
+    g = _gen(seed)
+    q = normal((B, Hq, PREFIX, d), 1.0, g)
+    k = normal((B, Hkv, PREFIX, d), 1.0, g)
+    v = normal((B, Hkv, PREFIX, d), 1.0, g)
+    return AttnCase("causal", q, k, v, L=PREFIX, block=PREFIX)
+
+
+def multimodal_step(step: int, n: int, B: int = 2, Hq: int = 32, Hkv: int = 8, d: int = 128,
+                    V: int = VOCAB, sigma: float = 3.0):
+    """Per denoise step ``step`` (seed 100+step): the active block's queries,
+    its fresh K/V rows (written into the cache at the block's position) and
+    the canvas logits [B, n, V] with planted peaks."""
+    g = _gen(100 + step)
+    q = normal((B, Hq, n, d), 1.0, g)
+    kb = normal((B, Hkv, n, d), 1.0, g)
+    vb = normal((B, Hkv, n, d), 1.0, g)
+    logits, idx = planted_logits(B, n, V, sigma, g)
+    return q, kb, vb, logits, idx

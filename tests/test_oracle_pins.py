@@ -1,0 +1,335 @@
+"""Pins of the CPU oracle against facts that do not depend on it.
+
+Each test checks the oracle against a closed form, a textbook routine (torch
+CPU fp64 scaled_dot_product_attention), a hand-derived fixture, or a brute
+force written differently (``oracle/brute.py``), so that a dropped term, a
+swapped half, a wrong inequality or a transposed operand in the oracle fails
+at least one of them.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle import brute
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_mask(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            rows.append([c == "1" for c in line.replace(" ", "")])
+    return np.array(rows, dtype=bool)
+
+
+def _rand(shape, seed, dtype=torch.float32):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(*shape, generator=g, dtype=torch.float32).to(dtype)
+
+
+def _sdpa(q, k, v, mask=None, causal=False):
+    """torch CPU fp64 SDPA on [B,H,S,d] with repeat-interleaved kv heads."""
+    q, k, v = (torch.as_tensor(np.asarray(x, dtype=np.float64)) for x in (q, k, v))
+    G = q.shape[1] // k.shape[1]
+    k = k.repeat_interleave(G, dim=1)
+    v = v.repeat_interleave(G, dim=1)
+    m = None if mask is None else torch.as_tensor(mask)
+    return F.scaled_dot_product_attention(q, k, v, attn_mask=m, is_causal=causal).numpy()
+
+
+# ---------------------------------------------------------------- masks
+
+@pytest.mark.parametrize("L", range(1, 13))
+def test_hybrid_mask_three_constructions(L):
+    for b in range(1, L + 1):
+        M = oracle.mask("hybrid", L, b)
+        kron = np.array(brute.hybrid_mask_kron(L, b), dtype=bool)
+        enum = np.array(brute.hybrid_mask_enum(L, b), dtype=bool)
+        assert (M == kron).all(), (L, b)
+        assert (M == enum).all(), (L, b)
+        assert M[np.arange(2 * L), np.arange(2 * L)].all()   # every row sees itself
+        assert not M[L:, :L].any()                            # x_0 never sees x_t
+
+
+def test_mask_golden_fixtures():
+    assert (oracle.mask("hybrid", 6, 2) == _read_mask("hybrid_mask_L6_b2.txt")).all()
+    assert (oracle.mask("hybrid", 5, 2) == _read_mask("hybrid_mask_L5_b2.txt")).all()
+    assert (oracle.mask("causal", 6, 3) == _read_mask("causal_mask_L6_n3.txt")).all()
+
+
+@pytest.mark.parametrize("L,n", [(1, 1), (5, 1), (5, 5), (9, 4), (33, 28)])
+def test_decode_causal_masks(L, n):
+    assert (oracle.mask("decode", L, n) == np.array(brute.decode_mask_enum(L, n), bool)).all()
+    assert (oracle.mask("causal", L, n) == np.array(brute.causal_mask_enum(L, n), bool)).all()
+
+
+def test_pair_counts_closed_form():
+    for L in (1, 7, 16, 64, 100):
+        for b in sorted({1, 2, 3, 4, 7, 32, L} & set(range(1, L + 1))):
+            starts = range(0, L, b)
+            closed = 2 * sum(min(b, L - s) * (s + min(b, L - s)) for s in starts)
+            assert oracle.pair_count("hybrid", L, b) == closed
+            if L % b == 0:
+                assert closed == L * (L + b)
+    for L, n in ((10, 3), (64, 64), (4124, 28)):
+        assert oracle.pair_count("decode", L, n) == n * L
+        assert oracle.pair_count("causal", L, n) == n * (L - n) + n * (n + 1) // 2
+    # the training-form workload: L=2048, b=32 -> L(L+b) pairs per head
+    assert 2048 * (2048 + 32) * 4 * 128 * 4 * 32 == 279172874240
+
+
+# ---------------------------------------------------------------- attention
+
+def _hybrid_inputs(L, d=8, Hq=2, Hkv=1, B=1, seed=0):
+    q = _rand((B, Hq, 2 * L, d), seed)
+    k = _rand((B, Hkv, 2 * L, d), seed + 1)
+    v = _rand((B, Hkv, 2 * L, d), seed + 2)
+    return q, k, v
+
+
+def test_block1_is_causal():
+    L = 24
+    q, k, v = _hybrid_inputs(L, Hq=4, Hkv=2)
+    out = oracle.attention("hybrid", q, k, v, L, 1)
+    ref0 = _sdpa(q[:, :, L:], k[:, :, L:], v[:, :, L:], causal=True)
+    np.testing.assert_allclose(out[:, :, L:], ref0, rtol=0, atol=1e-12)
+    # x_t half equals causal attention over x_0 once x_t's keys/values equal x_0's
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, :L] = k[:, :, L:]
+    v2[:, :, :L] = v[:, :, L:]
+    out2 = oracle.attention("hybrid", q, k2, v2, L, 1)
+    ref_t = _sdpa(q[:, :, :L], k[:, :, L:], v[:, :, L:], causal=True)
+    np.testing.assert_allclose(out2[:, :, :L], ref_t, rtol=0, atol=1e-12)
+
+
+def test_block_L_is_per_half_bidirectional():
+    L = 20
+    q, k, v = _hybrid_inputs(L, Hq=2, Hkv=2)
+    out = oracle.attention("hybrid", q, k, v, L, L)
+    np.testing.assert_allclose(out[:, :, :L], _sdpa(q[:, :, :L], k[:, :, :L], v[:, :, :L]), atol=1e-12, rtol=0)
+    np.testing.assert_allclose(out[:, :, L:], _sdpa(q[:, :, L:], k[:, :, L:], v[:, :, L:]), atol=1e-12, rtol=0)
+
+
+def test_decode_is_unmasked_sdpa():
+    q = _rand((2, 4, 5, 16), 3)
+    k = _rand((2, 2, 37, 16), 4)
+    v = _rand((2, 2, 37, 16), 5)
+    out = oracle.attention("decode", q, k, v, 37, 5)
+    np.testing.assert_allclose(out, _sdpa(q, k, v), atol=1e-12, rtol=0)
+
+
+def test_causal_is_bottom_right_sdpa():
+    n, L = 7, 40
+    q = _rand((1, 4, n, 16), 6)
+    k = _rand((1, 1, L, 16), 7)
+    v = _rand((1, 1, L, 16), 8)
+    out = oracle.attention("causal", q, k, v, L, n)
+    br = torch.ones(n, L, dtype=torch.bool).tril(diagonal=L - n)
+    np.testing.assert_allclose(out, _sdpa(q, k, v, mask=br), atol=1e-12, rtol=0)
+    # top-left alignment would differ: guard against that reading
+    assert not np.allclose(out, _sdpa(q, k, v, causal=True), atol=1e-6)
+
+
+def test_cross_mode_identities():
+    L, b = 21, 5
+    q, k, v = _hybrid_inputs(L, Hq=4, Hkv=2, seed=11)
+    out = oracle.attention("hybrid", q, k, v, L, b)
+    for s in range(0, L, b):
+        e = min(L, s + b)
+        # noisy block = decode over (clean blocks before it) + (that noisy block)
+        kk = torch.cat([k[:, :, L:L + s], k[:, :, s:e]], dim=2)
+        vv = torch.cat([v[:, :, L:L + s], v[:, :, s:e]], dim=2)
+        dec = oracle.attention("decode", q[:, :, s:e], kk, vv, kk.shape[2], e - s)
+        np.testing.assert_allclose(out[:, :, s:e], dec, atol=1e-12, rtol=0)
+        # clean block = decode over clean blocks up to and including it
+        kk = k[:, :, L:L + e]
+        vv = v[:, :, L:L + e]
+        dec = oracle.attention("decode", q[:, :, L + s:L + e], kk, vv, e, e - s)
+        np.testing.assert_allclose(out[:, :, L + s:L + e], dec, atol=1e-12, rtol=0)
+    # causal(L, n) = last n rows of causal(L, L)
+    qc = _rand((1, 2, 30, 8), 12)
+    kc = _rand((1, 2, 30, 8), 13)
+    vc = _rand((1, 2, 30, 8), 14)
+    full = oracle.attention("causal", qc, kc, vc, 30, 30)
+    part = oracle.attention("causal", qc[:, :, -6:], kc, vc, 30, 6)
+    np.testing.assert_allclose(part, full[:, :, -6:], atol=1e-12, rtol=0)
+    # GQA = MHA with repeat-interleaved kv heads (head h uses kv head h // G)
+    mha = oracle.attention("hybrid", q, k.repeat_interleave(2, 1), v.repeat_interleave(2, 1), L, b)
+    np.testing.assert_allclose(out, mha, atol=0, rtol=0)
+
+
+def test_weights_rows_sum_to_one_and_masked_are_zero():
+    # With V = identity over the keys, each output row IS the weight row.
+    for mode, L, b in (("hybrid", 9, 2), ("hybrid", 8, 3), ("causal", 12, 5), ("decode", 7, 3)):
+        rows = 2 * L if mode == "hybrid" else b
+        keys = 2 * L if mode == "hybrid" else L
+        q = _rand((1, 1, rows, 4), 20)
+        k = _rand((1, 1, keys, 4), 21)
+        v = torch.eye(keys).reshape(1, 1, keys, keys)
+        q4 = torch.nn.functional.pad(q, (0, keys - 4))        # d = keys; zero-pad keeps q.k
+        k4 = torch.nn.functional.pad(k, (0, keys - 4))
+        W = oracle.attention(mode, q4, k4, v, L, b)[0, 0]
+        M = oracle.mask(mode, L, b)
+        np.testing.assert_allclose(W.sum(axis=1), 1.0, atol=1e-12, rtol=0)
+        assert (W[~M] == 0.0).all()
+        assert (W[M] > 0.0).all()
+
+
+def test_masked_perturbation_changes_nothing():
+    L, b = 16, 4
+    q, k, v = _hybrid_inputs(L, Hq=2, Hkv=1, seed=30)
+    M = oracle.mask("hybrid", L, b)
+    base = oracle.attention("hybrid", q, k, v, L, b)
+    for qb in range(0, 2 * L, b):
+        rows = slice(qb, qb + b)
+        seen = M[rows].any(axis=0)
+        k2, v2 = k.clone(), v.clone()
+        noise = _rand(k.shape, 31 + qb) * 1e4
+        k2[:, :, ~torch.as_tensor(seen)] = noise[:, :, ~torch.as_tensor(seen)]
+        v2[:, :, ~torch.as_tensor(seen)] = -noise[:, :, ~torch.as_tensor(seen)]
+        out = oracle.attention("hybrid", q, k2, v2, L, b)
+        assert np.array_equal(out[:, :, rows], base[:, :, rows])
+
+
+def test_closed_forms():
+    L, b = 10, 3
+    q, k, _ = _hybrid_inputs(L, seed=40)
+    v = torch.full((1, 1, 2 * L, 8), 0.0)
+    v[..., :] = torch.arange(8, dtype=torch.float32)           # every value row identical
+    out = oracle.attention("hybrid", q, k, v, L, b)
+    np.testing.assert_allclose(out, np.broadcast_to(np.arange(8.0), out.shape), atol=1e-12, rtol=0)
+    # identical keys -> uniform weights -> mean of the visible value rows
+    k1 = torch.ones_like(k) * 0.5
+    v1 = _rand((1, 1, 2 * L, 8), 41)
+    out = oracle.attention("hybrid", q, k1, v1, L, b)
+    M = oracle.mask("hybrid", L, b)
+    ref = np.stack([v1[0, 0].numpy()[M[i]].astype(np.float64).mean(axis=0) for i in range(2 * L)])
+    np.testing.assert_allclose(out[0, 0], ref, atol=1e-12, rtol=0)
+
+
+def test_brute_loops_agree():
+    L, b, d = 6, 4, 5
+    q, k, v = _hybrid_inputs(L, d=d, seed=50)
+    out = oracle.attention("hybrid", q, k, v, L, b)[0, 0]
+    M = brute.hybrid_mask_enum(L, b)
+    ref = brute.attention_loops(q[0, 0].double().tolist(), k[0, 0].double().tolist(),
+                                v[0, 0].double().tolist(), M, 1 / math.sqrt(d))
+    np.testing.assert_allclose(out, np.array(ref), atol=1e-13, rtol=0)
+
+
+# ---------------------------------------------------------------- commit
+
+def _commit(logits, masked, tau, k_min, tokens=None):
+    G, R, _ = logits.shape
+    if tokens is None:
+        tokens = np.full((G, R), -7, dtype=np.int64)
+    return oracle.commit(logits, masked, tokens, tau, k_min)
+
+
+def test_commit_uniform_row_probability():
+    for V in (1, 2, 4, 1000, 131072):
+        lg = np.full((1, 1, V), 0.375, dtype=np.float32)
+        _, _, info = _commit(lg, np.ones((1, 1), np.uint8), 0.5, 0)
+        assert info["p64"][0, 0] == pytest.approx(1.0 / V, rel=1e-12)
+        assert info["argmax"][0, 0] == 0                         # ties -> lowest id
+
+
+def test_commit_single_peak_closed_form_and_threshold_side():
+    V, tau = 1000, 0.85
+    for side in (+1e-3, -1e-3):
+        target = tau + side
+        delta = math.log((V - 1) * target / (1 - target))        # p = 1/(1+(V-1)e^-delta)
+        lg = np.zeros((1, 1, V), dtype=np.float32)
+        lg[0, 0, 417] = np.float32(delta)
+        toks, m, info = _commit(lg, np.ones((1, 1), np.uint8), tau, 0)
+        p_closed = 1.0 / (1.0 + (V - 1) * math.exp(-float(np.float32(delta))))
+        assert info["p64"][0, 0] == pytest.approx(p_closed, rel=1e-12)
+        committed = side > 0
+        assert (m[0, 0] == 0) == committed
+        assert (toks[0, 0] == 417) == committed
+
+
+def test_commit_strict_threshold():
+    lg = np.zeros((1, 2, 4), dtype=np.float32)                   # p = 0.25 exactly
+    t, m, _ = _commit(lg, np.ones((1, 2), np.uint8), 0.25, 0)
+    assert m.tolist() == [[1, 1]] and t.tolist() == [[-7, -7]]
+    t, m, _ = _commit(lg, np.ones((1, 2), np.uint8), float(np.nextafter(np.float32(0.25), 0)), 0)
+    assert m.tolist() == [[0, 0]] and t.tolist() == [[0, 0]]
+
+
+def test_commit_argmax_ties_lowest_index():
+    lg = np.zeros((1, 3, 50), dtype=np.float32)
+    lg[0, 0, [7, 9, 30]] = 5.0
+    lg[0, 1, [49, 48]] = 2.5
+    lg[0, 2, [0, 1]] = 1.0
+    t, m, info = _commit(lg, np.ones((1, 3), np.uint8), 0.0, 0)
+    assert info["argmax"][0].tolist() == [7, 48, 0]
+    assert t[0].tolist() == [7, 48, 0] and m[0].tolist() == [0, 0, 0]
+
+
+def test_commit_brute_force_subsets():
+    rng = np.random.default_rng(123)
+    for trial in range(120):
+        R = int(rng.integers(1, 13))
+        V = int(rng.integers(2, 40))
+        lg = (rng.standard_normal((1, R, V)) * rng.uniform(0.5, 6)).astype(np.float32)
+        if trial % 5 == 0:                 # plant exact probability ties across rows
+            lg[0, R // 2] = lg[0, 0]
+        masked = (rng.random((1, R)) < 0.7).astype(np.uint8)
+        tau = float(np.float32(rng.uniform(0.05, 0.95)))
+        k_min = int(rng.integers(0, R + 3))
+        tokens0 = np.full((1, R), -7, dtype=np.int64)
+        t, m, info = oracle.commit(lg, masked, tokens0, tau, k_min)
+        p32 = [float(np.float32(x)) if masked[0, r] else 0.0 for r, x in enumerate(info["p64"][0])]
+        S = brute.commit_subset(p32, masked[0].tolist(), tau, k_min)
+        committed = tuple(r for r in range(R) if masked[0, r] and not m[0, r])
+        assert committed == S, (trial, committed, S)
+        for r in range(R):
+            lg64 = lg[0, r].astype(np.float64)
+            if r in S:
+                assert t[0, r] == int(np.flatnonzero(lg64 == lg64.max())[0])
+            else:
+                assert t[0, r] == -7 and m[0, r] == masked[0, r]
+
+
+def test_commit_groups_are_independent_and_kmin_saturates():
+    rng = np.random.default_rng(5)
+    lg = rng.standard_normal((3, 6, 30)).astype(np.float32)
+    masked = np.array([[1, 1, 0, 1, 0, 1], [0, 0, 0, 0, 0, 0], [1, 1, 1, 1, 1, 1]], np.uint8)
+    t, m, _ = _commit(lg, masked, 0.999, 100)       # k_min above #masked -> all masked commit
+    assert not m.any()
+    assert (t[1] == -7).all()
+    t, m, _ = _commit(lg, masked, 0.999, 1)
+    assert (masked - m).sum(axis=1).tolist() == [1, 0, 1]
+
+
+# ---------------------------------------------------------------- verify
+
+def test_verify_planted_prefix():
+    import synth
+    g = torch.Generator().manual_seed(99)
+    logits, idx = synth.planted_logits(6, 10, 300, 3.0, g, dtype=torch.float32)
+    drafts, acc = synth.verify_drafts(idx, seed=3, p=0.3, V=300)
+    am, accept = oracle.verify(logits, drafts)
+    assert (am == idx.numpy()).all()
+    assert accept.tolist() == acc.tolist()
+    d2 = idx.numpy().copy()                  # all drafts right -> R
+    am, accept = oracle.verify(logits, d2)
+    assert accept.tolist() == [10] * 6
+
+
+def test_tile_class_reduction():
+    M = oracle.mask("hybrid", 8, 2)
+    assert oracle.tile_class(M, 0, 2, 0, 2) == oracle.FULL
+    assert oracle.tile_class(M, 0, 2, 2, 4) == oracle.EMPTY
+    assert oracle.tile_class(M, 0, 4, 0, 4) == oracle.PARTIAL
+    assert oracle.tile_class(M, 8, 16, 0, 8) == oracle.EMPTY
