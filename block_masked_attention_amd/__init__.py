@@ -1,0 +1,189 @@
+"""Block-diffusion attention and the confidence commit on MI355X (gfx950).
+
+A thin ctypes binding over ``libbda.so`` (C ABI declared in ``include/bda.h``).
+Tensors are torch CUDA (HIP) tensors; this module only checks dtypes, shapes
+and devices, allocates outputs/workspaces with torch, and passes raw device
+pointers plus torch's current HIP stream to the library.  Every step of the
+computation runs in the library's kernels.  There is no CPU fallback: if the
+library is missing, importing this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbda.so")
+
+MODE = {"hybrid": 0, "decode": 1, "causal": 2}
+BF16, F32 = 0, 1
+TILE_FULL, TILE_EMPTY, TILE_PARTIAL = 0, 1, 2
+
+_ENTRY_POINTS = (
+    "bda_attn_fwd", "bda_attn_workspace_bytes", "bda_commit", "bda_commit_workspace_bytes",
+    "bda_verify", "bda_verify_workspace_bytes", "bda_classify_tile", "bda_strerror",
+    "bda_last_error", "bda_version",
+)
+
+
+class BdaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {lib.bda_strerror(code).decode()} ({lib.bda_last_error().decode()})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m block_masked_attention_amd.build` "
+                          "(or __graft_entry__.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, S, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    L.bda_attn_fwd.argtypes = [P, P, P, P, I, I, I, I, I, I, I, P, S, P]
+    L.bda_attn_fwd.restype = I
+    L.bda_attn_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    L.bda_attn_workspace_bytes.restype = S
+    L.bda_commit.argtypes = [P, I, P, P, F, I, I, I, I, P, S, P]
+    L.bda_commit.restype = I
+    L.bda_commit_workspace_bytes.argtypes = [I, I, I]
+    L.bda_commit_workspace_bytes.restype = S
+    L.bda_verify.argtypes = [P, I, P, P, P, I, I, I, P, S, P]
+    L.bda_verify.restype = I
+    L.bda_verify_workspace_bytes.argtypes = [I, I, I]
+    L.bda_verify_workspace_bytes.restype = S
+    L.bda_classify_tile.argtypes = [I, I, I, I, I, I, I]
+    L.bda_classify_tile.restype = I
+    for name in ("bda_strerror",):
+        getattr(L, name).argtypes = [I]
+        getattr(L, name).restype = ctypes.c_char_p
+    for name in ("bda_last_error", "bda_version"):
+        getattr(L, name).argtypes = []
+        getattr(L, name).restype = ctypes.c_char_p
+    return L
+
+
+lib = _load()
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _check_dev(*ts):
+    dev = ts[0].device
+    for t in ts:
+        if t is None:
+            continue
+        if t.device.type != "cuda" or t.device != dev:
+            raise ValueError("all tensors must be on the same HIP device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    return dev
+
+
+def _workspace(nbytes: int, device, ws):
+    if nbytes == 0:
+        return None
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError(f"workspace needs {nbytes} bytes")
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def attn_workspace_bytes(B, Hq, Hkv, L, d, block, mode) -> int:
+    return int(lib.bda_attn_workspace_bytes(B, Hq, Hkv, L, d, block, MODE[mode] if isinstance(mode, str) else mode))
+
+
+def attn_fwd(q, k, v, mode: str, block: int, out=None, workspace=None):
+    """Masked attention forward (bf16).  HYBRID: q/k/v [B,H,2L,d] over
+    [x_t ; x_0]; DECODE/CAUSAL: q [B,Hq,n,d] with n = ``block`` and k/v
+    [B,Hkv,L,d].  Returns ``out`` shaped like q."""
+    m = MODE[mode]
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or t.dim() != 4:
+            raise ValueError("q, k, v must be 4-D bfloat16")
+    dev = _check_dev(q, k, v)
+    B, Hq, Sq, d = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k/v shape mismatch")
+    if m == 0:
+        if Sq != Sk or Sq % 2:
+            raise ValueError("hybrid form needs q, k, v of 2L rows")
+        L = Sq // 2
+    else:
+        if Sq != block:
+            raise ValueError("decode/causal: q rows must equal block")
+        L = Sk
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != torch.bfloat16:
+        raise ValueError("out must match q")
+    _check_dev(q, out)
+    need = attn_workspace_bytes(B, Hq, Hkv, L, d, block, m)
+    ws = _workspace(need, dev, workspace)
+    rc = lib.bda_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, L, d, block, m,
+                          _ptr(ws), need, _stream(dev))
+    if rc:
+        raise BdaError(rc, "bda_attn_fwd")
+    return out
+
+
+def commit(logits, tokens, masked, threshold: float, k_min: int, workspace=None):
+    """In-place confidence commit on logits [G,R,V] (bf16 or fp32);
+    ``tokens`` int64 [G,R] and ``masked`` uint8 [G,R] are updated."""
+    if logits.dim() != 3:
+        raise ValueError("logits must be [G, R, V]")
+    G, R, V = logits.shape
+    dt = {torch.bfloat16: BF16, torch.float32: F32}.get(logits.dtype)
+    if dt is None:
+        raise ValueError("logits must be bfloat16 or float32")
+    if tokens.dtype != torch.int64 or masked.dtype != torch.uint8:
+        raise ValueError("tokens int64, masked uint8")
+    if tuple(tokens.shape) != (G, R) or tuple(masked.shape) != (G, R):
+        raise ValueError("tokens/masked must be [G, R]")
+    dev = _check_dev(logits, tokens, masked)
+    need = int(lib.bda_commit_workspace_bytes(G, R, V))
+    ws = _workspace(need, dev, workspace)
+    rc = lib.bda_commit(_ptr(logits), dt, _ptr(tokens), _ptr(masked), float(threshold), int(k_min),
+                        G, R, V, _ptr(ws), need, _stream(dev))
+    if rc:
+        raise BdaError(rc, "bda_commit")
+    return tokens, masked
+
+
+def verify(logits, drafts, workspace=None):
+    """Argmax per row and longest matching prefix: returns (argmax [B,R]
+    int64, accept_len [B] int32)."""
+    if logits.dim() != 3:
+        raise ValueError("logits must be [B, R, V]")
+    B, R, V = logits.shape
+    dt = {torch.bfloat16: BF16, torch.float32: F32}.get(logits.dtype)
+    if dt is None:
+        raise ValueError("logits must be bfloat16 or float32")
+    if drafts.dtype != torch.int64 or tuple(drafts.shape) != (B, R):
+        raise ValueError("drafts must be int64 [B, R]")
+    dev = _check_dev(logits, drafts)
+    am = torch.empty(B, R, dtype=torch.int64, device=dev)
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    need = int(lib.bda_verify_workspace_bytes(B, R, V))
+    ws = _workspace(need, dev, workspace)
+    rc = lib.bda_verify(_ptr(logits), dt, _ptr(drafts), _ptr(am), _ptr(acc), B, R, V,
+                        _ptr(ws), need, _stream(dev))
+    if rc:
+        raise BdaError(rc, "bda_verify")
+    return am, acc
+
+
+def classify_tile(mode, L, block, q0, q1, k0, k1) -> int:
+    return int(lib.bda_classify_tile(MODE[mode] if isinstance(mode, str) else mode, L, block, q0, q1, k0, k1))
+
+
+def version() -> str:
+    return lib.bda_version().decode()

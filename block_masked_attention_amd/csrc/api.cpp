@@ -1,0 +1,183 @@
+// C ABI of libbda: argument validation, error reporting, dispatch to the
+// kernel launchers.  Validation always runs on the host before any launch.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/bda.h"
+#include "geometry.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return BDA_OK;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const char* x = (const char*)a;
+  const char* y = (const char*)b;
+  return x < y + nb && y < x + na;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_attn(int B, int Hq, int Hkv, int L, int d, int block, int mode) {
+  if (mode < BDA_MODE_HYBRID || mode > BDA_MODE_CAUSAL) return fail(BDA_EINVAL, "mode %d is not one of 0,1,2", mode);
+  if (B < 1 || Hq < 1 || Hkv < 1 || L < 1) return fail(BDA_EINVAL, "B, Hq, Hkv and L must be >= 1");
+  if (Hq % Hkv) return fail(BDA_EINVAL, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (d != 32 && d != 64 && d != 128) return fail(BDA_EUNSUPPORTED, "head dim %d not in {32, 64, 128}", d);
+  if (block < 1 || block > L) return fail(BDA_EINVAL, "block %d must be in [1, L=%d]", block, L);
+  if (L > (1 << 28)) return fail(BDA_EUNSUPPORTED, "L %d above 2^28", L);
+  return BDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bda_strerror(int code) {
+  switch (code) {
+    case BDA_OK: return "ok";
+    case BDA_EINVAL: return "invalid argument";
+    case BDA_EUNSUPPORTED: return "unsupported configuration";
+    case BDA_EWORKSPACE: return "workspace missing or too small";
+    case BDA_EHIP: return "HIP runtime error";
+    default: return "unknown error code";
+  }
+}
+
+const char* bda_last_error(void) { return g_err; }
+
+const char* bda_version(void) { return "bda 0.1 (gfx950)"; }
+
+size_t bda_attn_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int block, int mode) {
+  if (check_attn(B, Hq, Hkv, L, d, block, mode)) return 0;
+  bda::AttnPlan p;
+  const char* why = "";
+  if (bda::attn_make_plan(B, Hq, Hkv, L, d, block, mode, &p, &why)) return 0;
+  return p.ws_bytes;
+}
+
+int bda_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv,
+                 int L, int d, int block, int mode, void* workspace, size_t ws_bytes, void* stream) {
+  if (int e = check_attn(B, Hq, Hkv, L, d, block, mode)) return e;
+  if (!q || !k || !v || !out) return fail(BDA_EINVAL, "q, k, v and out must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(BDA_EINVAL, "q, k, v and out must be 16-byte aligned");
+  const size_t Sq = mode == BDA_MODE_HYBRID ? 2 * (size_t)L : (size_t)block;
+  const size_t Sk = mode == BDA_MODE_HYBRID ? 2 * (size_t)L : (size_t)L;
+  const size_t qbytes = (size_t)B * Hq * Sq * d * 2;
+  const size_t kbytes = (size_t)B * Hkv * Sk * d * 2;
+  if (overlap(out, qbytes, q, qbytes) || overlap(out, qbytes, k, kbytes) || overlap(out, qbytes, v, kbytes))
+    return fail(BDA_EINVAL, "out overlaps q, k or v");
+  bda::AttnPlan p;
+  const char* why = "";
+  if (int e = bda::attn_make_plan(B, Hq, Hkv, L, d, block, mode, &p, &why))
+    return fail(e == 2 ? BDA_EUNSUPPORTED : BDA_EINVAL, "%s", why);
+  if (p.ws_bytes) {
+    if (!workspace || ws_bytes < p.ws_bytes)
+      return fail(BDA_EWORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_bytes,
+                  workspace ? ws_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(BDA_EINVAL, "workspace must be 16-byte aligned");
+    if (overlap(workspace, p.ws_bytes, out, qbytes) || overlap(workspace, p.ws_bytes, q, qbytes) ||
+        overlap(workspace, p.ws_bytes, k, kbytes) || overlap(workspace, p.ws_bytes, v, kbytes))
+      return fail(BDA_EINVAL, "workspace overlaps a tensor argument");
+  }
+  hipError_t e = bda::attn_launch(p, q, k, v, out, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BDA_EHIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+static int check_logits(const void* logits, int dtype, int G, int R, int V, const char* gname) {
+  if (dtype != BDA_BF16 && dtype != BDA_F32) return fail(BDA_EINVAL, "dtype %d is not BDA_BF16 or BDA_F32", dtype);
+  if (G < 0 || R < 0) return fail(BDA_EINVAL, "%s and R must be >= 0", gname);
+  if (V < 1) return fail(BDA_EINVAL, "V must be >= 1");
+  if ((size_t)G * R > (size_t)0x7fffffff / 64) return fail(BDA_EUNSUPPORTED, "too many rows");
+  if ((size_t)G * R > 0 && !logits) return fail(BDA_EINVAL, "logits must be non-NULL");
+  return BDA_OK;
+}
+
+size_t bda_commit_workspace_bytes(int G, int R, int V) {
+  if (G < 0 || R < 0 || V < 1) return 0;
+  bda::CommitPlan p;
+  bda::commit_make_plan(G, R, V, 0, &p);
+  return p.ws_bytes;
+}
+
+int bda_commit(const void* logits, int dtype, int64_t* tokens, uint8_t* masked, float threshold,
+               int k_min, int G, int R, int V, void* workspace, size_t ws_bytes, void* stream) {
+  if (int e = check_logits(logits, dtype, G, R, V, "G")) return e;
+  if (k_min < 0) return fail(BDA_EINVAL, "k_min must be >= 0");
+  if (isnan(threshold)) return fail(BDA_EINVAL, "threshold is NaN");
+  const size_t rows = (size_t)G * R;
+  if (rows == 0) return ok();
+  if (!tokens || !masked) return fail(BDA_EINVAL, "tokens and masked must be non-NULL");
+  const size_t lbytes = rows * V * (dtype == BDA_BF16 ? 2 : 4);
+  if (overlap(tokens, rows * 8, logits, lbytes) || overlap(masked, rows, logits, lbytes) ||
+      overlap(tokens, rows * 8, masked, rows))
+    return fail(BDA_EINVAL, "tokens, masked and logits must not overlap");
+  bda::CommitPlan p;
+  bda::commit_make_plan(G, R, V, dtype, &p);
+  if (!workspace || ws_bytes < p.ws_bytes)
+    return fail(BDA_EWORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_bytes,
+                workspace ? ws_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(BDA_EINVAL, "workspace must be 16-byte aligned");
+  if (overlap(workspace, p.ws_bytes, logits, lbytes) || overlap(workspace, p.ws_bytes, tokens, rows * 8) ||
+      overlap(workspace, p.ws_bytes, masked, rows))
+    return fail(BDA_EINVAL, "workspace overlaps a tensor argument");
+  hipError_t e = bda::commit_launch(p, logits, tokens, masked, threshold, k_min, workspace,
+                                    (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BDA_EHIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t bda_verify_workspace_bytes(int B, int R, int V) { return bda_commit_workspace_bytes(B, R, V); }
+
+int bda_verify(const void* logits, int dtype, const int64_t* drafts, int64_t* argmax_out,
+               int32_t* accept_len, int B, int R, int V, void* workspace, size_t ws_bytes,
+               void* stream) {
+  if (int e = check_logits(logits, dtype, B, R, V, "B")) return e;
+  if (B == 0) return ok();
+  if (!accept_len) return fail(BDA_EINVAL, "accept_len must be non-NULL");
+  const size_t rows = (size_t)B * R;
+  if (rows && (!drafts || !argmax_out)) return fail(BDA_EINVAL, "drafts and argmax_out must be non-NULL");
+  const size_t lbytes = rows * V * (dtype == BDA_BF16 ? 2 : 4);
+  if (rows && (overlap(argmax_out, rows * 8, logits, lbytes) || overlap(argmax_out, rows * 8, drafts, rows * 8) ||
+               overlap(accept_len, (size_t)B * 4, logits, lbytes) ||
+               overlap(accept_len, (size_t)B * 4, argmax_out, rows * 8)))
+    return fail(BDA_EINVAL, "outputs must not overlap inputs or each other");
+  bda::CommitPlan p;
+  bda::commit_make_plan(B, R, V, dtype, &p);
+  if (!workspace || ws_bytes < p.ws_bytes)
+    return fail(BDA_EWORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_bytes,
+                workspace ? ws_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(BDA_EINVAL, "workspace must be 16-byte aligned");
+  hipError_t e = bda::verify_launch(p, logits, drafts, argmax_out, accept_len, workspace,
+                                    (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BDA_EHIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int bda_classify_tile(int mode, int L, int block, int q0, int q1, int k0, int k1) {
+  if (mode < 0 || mode > 2 || L < 1 || block < 1 || block > L) return -1;
+  const int rows = mode == BDA_MODE_HYBRID ? 2 * L : block;
+  const int keys = mode == BDA_MODE_HYBRID ? 2 * L : L;
+  if (q0 < 0 || q1 < q0 || q1 > rows || k0 < 0 || k1 < k0 || k1 > keys) return -1;
+  return bda::classify_tile(mode, L, block, block, q0, q1, k0, k1);
+}
+
+}  // extern "C"

@@ -1,0 +1,342 @@
+// Confidence commit and speculative verify for gfx950.
+//
+// Confidence of a masked canvas position = its largest softmax probability
+// (SPRINT section of the LLaDA2.0-Uni summary); every position above the
+// threshold commits, with at least a per-step minimum number of commits
+// (same section, and the block-refinement scheduler of the DiffusionGemma
+// pipeline page, "Schedulers").  Verify takes each row's argmax and the
+// longest prefix that agrees with the drafts (linear speculative decoding,
+// sec. 2 of the Nemotron-Labs-Diffusion-8B-Base 3x analysis page).
+//
+// Pass 1 (stream): one workgroup per (row, vocabulary chunk) streams the
+// logits once with 16-byte non-temporal loads and keeps, per lane, the
+// running maximum m, the lowest index a reaching it and Z = sum exp(l - m)
+// (rescaled when m grows).  Lanes and wavefronts merge with the associative
+// rule  m = max(m1, m2);  Z = Z1 e^(m1-m) + Z2 e^(m2-m);  a = lowest index
+// among the maxima, in a fixed order, so results do not depend on timing.
+// Pass 2 (finalize): one workgroup per group merges the chunk partials of
+// its rows in chunk order, takes p = 1/Z, applies the threshold and the
+// minimum-count fallback, and writes tokens / masked.
+#include <limits.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace bda {
+
+constexpr int kCommitThreads = 256;
+constexpr int kChunk = 16384;            // vocabulary entries per streaming workgroup
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct Partial {
+  float m, z;
+  int a, pad;
+};
+
+struct Stat {
+  float m, z;
+  int a;
+};
+
+__device__ __forceinline__ Stat merge(Stat x, Stat y, bool with_z) {
+  Stat r;
+  r.m = fmaxf(x.m, y.m);
+  r.a = x.m > y.m ? x.a : (y.m > x.m ? y.a : min(x.a, y.a));
+  if (with_z) {
+    if (r.m == -INFINITY) {
+      r.z = 0.f;
+    } else {
+      r.z = x.z * exp2f((x.m - r.m) * kLog2e) + y.z * exp2f((y.m - r.m) * kLog2e);
+    }
+  } else {
+    r.z = 0.f;
+  }
+  return r;
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load_one(const void* row, int j) {
+  if (BF16) return __uint_as_float((unsigned)((const uint16_t*)row)[j] << 16);
+  return ((const float*)row)[j];
+}
+
+// Fold 8 values (indices base..base+7, increasing) into a lane's state.
+template <bool WITH_Z>
+__device__ __forceinline__ void fold8(Stat& s, const float (&x)[8], int base) {
+  float lm = x[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) lm = fmaxf(lm, x[e]);
+  if (lm > s.m) {
+    int idx = 7;
+#pragma unroll
+    for (int e = 6; e >= 0; --e) idx = x[e] == lm ? e : idx;
+    if (WITH_Z) s.z = s.m == -INFINITY ? 0.f : s.z * exp2f((s.m - lm) * kLog2e);
+    s.m = lm;
+    s.a = base + idx;
+  }
+  if (WITH_Z && s.m != -INFINITY) {
+    const float nb = -s.m * kLog2e;
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += exp2f(fmaf(x[e], kLog2e, nb));
+    s.z += acc;
+  }
+}
+
+template <bool BF16, bool WITH_Z>
+__global__ __launch_bounds__(kCommitThreads) void stream_kernel(const void* __restrict__ logits,
+                                                                const uint8_t* __restrict__ masked,
+                                                                Partial* __restrict__ part, int V,
+                                                                int n_chunks, int vec_ok) {
+  const int bid = blockIdx.x;
+  const int t = bid / n_chunks;
+  const int c = bid - t * n_chunks;
+  if (masked != nullptr && masked[t] == 0) return;
+  const int tid = threadIdx.x;
+  const size_t esz = BF16 ? 2 : 4;
+  const char* row = (const char*)logits + (size_t)t * V * esz;
+  const int c0 = c * kChunk;
+  const int c1 = min(V, c0 + kChunk);
+
+  Stat s{-INFINITY, 0.f, INT_MAX};
+  if (vec_ok) {
+    // 8 consecutive values per step: one 16-byte load (bf16) or two (fp32).
+    for (int base = c0 + 8 * tid; base < c1; base += 8 * kCommitThreads) {
+      float x[8];
+      if (base + 8 <= c1) {
+        if (BF16) {
+          const u32x4 w = __builtin_nontemporal_load((const u32x4*)(row + (size_t)base * 2));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[2 * e] = bf16_lo(w[e]);
+            x[2 * e + 1] = bf16_hi(w[e]);
+          }
+        } else {
+          const f32x4 w0 = __builtin_nontemporal_load((const f32x4*)(row + (size_t)base * 4));
+          const f32x4 w1 = __builtin_nontemporal_load((const f32x4*)(row + (size_t)base * 4 + 16));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[e] = w0[e];
+            x[4 + e] = w1[e];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = base + e < c1 ? load_one<BF16>(row, base + e) : -INFINITY;
+      }
+      fold8<WITH_Z>(s, x, base);
+    }
+  } else {
+    for (int base = c0 + 8 * tid; base < c1; base += 8 * kCommitThreads) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = base + e < c1 ? load_one<BF16>(row, base + e) : -INFINITY;
+      fold8<WITH_Z>(s, x, base);
+    }
+  }
+  // -INFINITY padding never wins a strict comparison, and contributes 0 to Z
+  // once a finite maximum exists.
+
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    Stat o;
+    o.m = __shfl_xor(s.m, off);
+    o.z = __shfl_xor(s.z, off);
+    o.a = __shfl_xor(s.a, off);
+    s = merge(s, o, WITH_Z);
+  }
+  __shared__ Stat wst[kCommitThreads / 64];
+  if ((tid & 63) == 0) wst[tid >> 6] = s;
+  __syncthreads();
+  if (tid == 0) {
+    Stat r = wst[0];
+#pragma unroll
+    for (int w = 1; w < kCommitThreads / 64; ++w) r = merge(r, wst[w], WITH_Z);
+    Partial p;
+    p.m = r.m;
+    p.z = r.z;
+    p.a = r.a;
+    p.pad = 0;
+    part[(size_t)t * n_chunks + c] = p;
+  }
+}
+
+__device__ __forceinline__ Stat row_stat(const Partial* part, size_t t, int n_chunks, bool with_z) {
+  Stat s{part[t * n_chunks].m, part[t * n_chunks].z, part[t * n_chunks].a};
+  for (int c = 1; c < n_chunks; ++c) {
+    const Partial& q = part[t * n_chunks + c];
+    s = merge(s, Stat{q.m, q.z, q.a}, with_z);
+  }
+  return s;
+}
+
+__device__ __forceinline__ int block_sum(int x, int* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  int s = 0;
+#pragma unroll
+  for (int w = 0; w < kCommitThreads / 64; ++w) s += red[w];
+  __syncthreads();
+  return s;
+}
+
+// One workgroup per group g.  rowp/rowa/rowf are workspace scratch [G*R].
+__global__ __launch_bounds__(kCommitThreads) void commit_finalize_kernel(
+    const Partial* __restrict__ part, int n_chunks, int64_t* __restrict__ tokens,
+    uint8_t* __restrict__ masked, float threshold, int k_min, int R, float* __restrict__ rowp,
+    int* __restrict__ rowa, uint8_t* __restrict__ rowf) {
+  __shared__ int red[kCommitThreads / 64];
+  const int g = blockIdx.x;
+  const size_t base = (size_t)g * R;
+  int nmask = 0, npass = 0;
+  for (int r = threadIdx.x; r < R; r += kCommitThreads) {
+    const size_t t = base + r;
+    uint8_t f = 0;
+    if (masked[t]) {
+      const Stat s = row_stat(part, t, n_chunks, true);
+      const float p = 1.f / s.z;
+      rowp[t] = p;
+      rowa[t] = s.a;
+      f = p > threshold ? 2 : 1;
+      nmask += 1;
+      npass += f == 2;
+    }
+    rowf[t] = f;
+  }
+  nmask = block_sum(nmask, red);
+  npass = block_sum(npass, red);
+  const int need = min(k_min, nmask) - npass;
+  __syncthreads();
+  for (int r = threadIdx.x; r < R; r += kCommitThreads) {
+    const size_t t = base + r;
+    const uint8_t f = rowf[t];
+    bool take = f == 2;
+    if (f == 1 && need > 0) {
+      // rank among masked rows below the threshold: larger p first, then lower row
+      const float p = rowp[t];
+      int rank = 0;
+      for (int o = 0; o < R && rank < need; ++o) {
+        if (rowf[base + o] != 1) continue;
+        const float po = rowp[base + o];
+        rank += (po > p) || (po == p && o < r);
+      }
+      take = rank < need;
+    }
+    if (take) {
+      tokens[t] = rowa[t];
+      masked[t] = 0;
+    }
+  }
+}
+
+// One workgroup per sequence: argmax per row, then the first disagreement.
+__global__ __launch_bounds__(kCommitThreads) void verify_finalize_kernel(
+    const Partial* __restrict__ part, int n_chunks, const int64_t* __restrict__ drafts,
+    int64_t* __restrict__ argmax_out, int32_t* __restrict__ accept, int R) {
+  __shared__ int red[kCommitThreads / 64];
+  const int b = blockIdx.x;
+  int first = R;
+  for (int r = threadIdx.x; r < R; r += kCommitThreads) {
+    const size_t t = (size_t)b * R + r;
+    const Stat s = row_stat(part, t, n_chunks, false);
+    argmax_out[t] = s.a;
+    if ((int64_t)s.a != drafts[t]) first = min(first, r);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) first = min(first, __shfl_xor(first, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = first;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int m = red[0];
+    for (int w = 1; w < kCommitThreads / 64; ++w) m = min(m, red[w]);
+    accept[b] = m;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// host side
+// ----------------------------------------------------------------------------
+
+int commit_make_plan(int G, int R, int V, int dtype, CommitPlan* p) {
+  CommitPlan x{};
+  x.G = G;
+  x.R = R;
+  x.V = V;
+  x.dtype = dtype;
+  x.chunk = kChunk;
+  x.n_chunks = (V + kChunk - 1) / kChunk;
+  const size_t rows = (size_t)G * R;
+  x.ws_bytes = rows * x.n_chunks * sizeof(Partial) + rows * (4 + 4 + 1) + 256;
+  *p = x;
+  return 0;
+}
+
+static void carve(const CommitPlan& p, void* ws, Partial** part, float** rowp, int** rowa,
+                  uint8_t** rowf) {
+  const size_t rows = (size_t)p.G * p.R;
+  char* c = (char*)ws;
+  *part = (Partial*)c;
+  c += rows * p.n_chunks * sizeof(Partial);
+  *rowp = (float*)c;
+  c += rows * 4;
+  *rowa = (int*)c;
+  c += rows * 4;
+  *rowf = (uint8_t*)c;
+}
+
+static bool vec_ok(const void* logits, int V, int dtype) {
+  const int per16 = dtype == 0 ? 8 : 4;
+  return ((uintptr_t)logits % 16) == 0 && V % per16 == 0;
+}
+
+template <bool WITH_Z>
+static hipError_t launch_stream(const CommitPlan& p, const void* logits, const uint8_t* masked,
+                                Partial* part, hipStream_t st) {
+  const long long grid = (long long)p.G * p.R * p.n_chunks;
+  const int vo = vec_ok(logits, p.V, p.dtype);
+  if (p.dtype == 0)
+    hipLaunchKernelGGL((stream_kernel<true, WITH_Z>), dim3((unsigned)grid), dim3(kCommitThreads), 0,
+                       st, logits, masked, part, p.V, p.n_chunks, vo);
+  else
+    hipLaunchKernelGGL((stream_kernel<false, WITH_Z>), dim3((unsigned)grid), dim3(kCommitThreads), 0,
+                       st, logits, masked, part, p.V, p.n_chunks, vo);
+  return hipGetLastError();
+}
+
+hipError_t commit_launch(const CommitPlan& p, const void* logits, int64_t* tokens, uint8_t* masked,
+                         float threshold, int k_min, void* ws, hipStream_t st) {
+  if ((long long)p.G * p.R == 0) return hipSuccess;
+  Partial* part;
+  float* rowp;
+  int* rowa;
+  uint8_t* rowf;
+  carve(p, ws, &part, &rowp, &rowa, &rowf);
+  (void)hipGetLastError();
+  hipError_t e = launch_stream<true>(p, logits, masked, part, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(commit_finalize_kernel, dim3(p.G), dim3(kCommitThreads), 0, st, part,
+                     p.n_chunks, tokens, masked, threshold, k_min, p.R, rowp, rowa, rowf);
+  return hipGetLastError();
+}
+
+hipError_t verify_launch(const CommitPlan& p, const void* logits, const int64_t* drafts,
+                         int64_t* argmax_out, int32_t* accept, void* ws, hipStream_t st) {
+  if (p.G == 0) return hipSuccess;
+  Partial* part;
+  float* rowp;
+  int* rowa;
+  uint8_t* rowf;
+  carve(p, ws, &part, &rowp, &rowa, &rowf);
+  (void)hipGetLastError();
+  if (p.R > 0) {
+    hipError_t e = launch_stream<false>(p, logits, nullptr, part, st);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(verify_finalize_kernel, dim3(p.G), dim3(kCommitThreads), 0, st, part,
+                     p.n_chunks, drafts, argmax_out, accept, p.R);
+  return hipGetLastError();
+}
+
+}  // namespace bda

@@ -1,0 +1,43 @@
+// Host-side plans and launchers shared between the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bda {
+
+// Work decomposition of one attention call.  Both the workspace query and the
+// launch derive it from the arguments alone, so they always agree.
+struct AttnPlan {
+  int mode, B, Hq, Hkv, G, L, n, blk, d;
+  int Sq, Sk;           // rows of the query / key tensors
+  int nw;               // wavefronts per workgroup (4 or 8)
+  int rows_per_wg;      // query rows per workgroup (per half in HYBRID)
+  int n_qtiles;         // query tiles per (batch, kv head)
+  int n_splits;         // key splits (DECODE/CAUSAL only; 1 = no combine)
+  int split_keys;       // keys per split, a multiple of the key tile
+  int pairs_per_xcd;    // >0: XCD-aware order of workgroups
+  long long grid;       // workgroups of the main kernel
+  size_t ws_bytes;      // workspace for split partials
+};
+
+int attn_make_plan(int B, int Hq, int Hkv, int L, int d, int block, int mode, AttnPlan* p,
+                   const char** why);
+hipError_t attn_launch(const AttnPlan& p, const void* q, const void* k, const void* v, void* out,
+                       void* ws, hipStream_t st);
+
+struct CommitPlan {
+  int G, R, V, dtype;
+  int chunk;            // vocabulary entries per streaming workgroup
+  int n_chunks;         // chunks per row
+  size_t ws_bytes;
+};
+
+int commit_make_plan(int G, int R, int V, int dtype, CommitPlan* p);
+hipError_t commit_launch(const CommitPlan& p, const void* logits, int64_t* tokens, uint8_t* masked,
+                         float threshold, int k_min, void* ws, hipStream_t st);
+hipError_t verify_launch(const CommitPlan& p, const void* logits, const int64_t* drafts,
+                         int64_t* argmax_out, int32_t* accept, void* ws, hipStream_t st);
+
+}  // namespace bda

@@ -1,0 +1,139 @@
+/*
+ * bda.h -- block-diffusion attention and the confidence commit on AMD Instinct
+ * MI355X (gfx950).  C ABI of libbda.so.
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer argument except `stream` is DEVICE memory owned by the
+ *    caller (allocated by whatever the caller uses, e.g. PyTorch).  The
+ *    library allocates nothing, frees nothing and keeps no state between
+ *    calls (the workspaces below are the caller's too).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the legacy default
+ *    stream).  Calls are asynchronous on that stream; the library never
+ *    synchronises.  Faults inside a kernel surface at the caller's next
+ *    synchronisation, not here.
+ *  - Tensors are dense, row-major, with the last index fastest.  bf16 is the
+ *    IEEE bfloat16 bit pattern stored in 16 bits.
+ *  - Arguments are validated on the host before any launch.  A non-zero
+ *    return is one of the BDA_E* codes below; bda_last_error() then holds a
+ *    detail string for the calling thread.  Nothing aborts, throws or prints.
+ *  - Outputs must not overlap inputs.  A workspace serves one call at a time.
+ *
+ * Citations name the pages the operations are defined on:
+ *  [NLD-3x]  "Analise do acelero de 3x do Nemotron-Labs-Diffusion-8B-Base"
+ *            (doido.pw): sec. 1 Block Diffusion Attention (hybrid mask
+ *            M_BD | M_OBC | M_BC, fused flex attention with a block mask),
+ *            sec. 2 Linear Speculative Decoding (bidirectional drafting,
+ *            causal validation, longest matching prefix).
+ *  [LLaDA]   "LLaDA2.0-Uni" summary (discuss.pytorch.kr): training objective
+ *            (BDLM conditioning of a noisy block on earlier clean blocks) and
+ *            SPRINT (confidence = top-1 softmax probability; accept every
+ *            position above tau with a per-step minimum).
+ *  [DGemma]  diffusers "DiffusionGemma" pipeline docs: intro (bidirectional
+ *            decoder over a canvas and a cached clean prefix), Schedulers
+ *            (threshold commit plus an even per-step share), the pipeline
+ *            call (logits [batch, canvas, vocab]; LongTensor sequences).
+ *  [VLM-8B]  "Nemotron-Labs-Diffusion-VLM-8B" usage page: generate() with
+ *            block_size 28 and threshold 0.85.
+ */
+#ifndef BDA_H
+#define BDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { BDA_MODE_HYBRID = 0, BDA_MODE_DECODE = 1, BDA_MODE_CAUSAL = 2 };
+enum { BDA_BF16 = 0, BDA_F32 = 1 };
+enum {
+    BDA_OK = 0,
+    BDA_EINVAL = 1,        /* bad pointer, size, shape or parameter          */
+    BDA_EUNSUPPORTED = 2,  /* valid request this build does not implement    */
+    BDA_EWORKSPACE = 3,    /* workspace missing or smaller than required     */
+    BDA_EHIP = 4           /* the HIP runtime reported an error at launch    */
+};
+enum { BDA_TILE_FULL = 0, BDA_TILE_EMPTY = 1, BDA_TILE_PARTIAL = 2 };
+
+/*
+ * Masked attention forward, one kernel family for the three forms.
+ * O = softmax(scale * Q K^T restricted to allowed keys) V, scale = 1/sqrt(d),
+ * bf16 inputs and output, fp32 accumulation.  Query head h reads kv head
+ * h / (Hq/Hkv) (grouped-query attention; Hq % Hkv == 0).  d in {32, 64, 128}.
+ *
+ * mode = BDA_MODE_HYBRID  ([NLD-3x] sec. 1; conditioning from [LLaDA]):
+ *   q, k, v, out are [B, H, 2L, d]; rows 0..L-1 are the noisy copy x_t,
+ *   rows L..2L-1 the clean copy x_0.  Positions are cut into blocks of
+ *   `block` (1 <= block <= L; the last block may be short).  An x_t query of
+ *   block j sees the x_t keys of block j and the x_0 keys of blocks < j; an
+ *   x_0 query of block j sees the x_0 keys of blocks <= j; x_0 queries never
+ *   see x_t keys.
+ * mode = BDA_MODE_DECODE  ([DGemma] intro; drafting in [NLD-3x] sec. 2):
+ *   q, out are [B, Hq, n, d] with n = block; k, v are [B, Hkv, L, d] whose
+ *   last n rows are the active block.  Every query sees all L keys.
+ * mode = BDA_MODE_CAUSAL  (validation in [NLD-3x] sec. 2):
+ *   shapes as DECODE; the n queries are the last n of the L positions, so
+ *   query i sees keys 0 .. L-n+i.  n = L is ordinary causal attention
+ *   (a prefill).
+ * workspace: device scratch of at least bda_attn_workspace_bytes(...) bytes
+ *   (may be NULL when that is 0); no initial contents are required.
+ */
+int bda_attn_fwd(const void* q, const void* k, const void* v, void* out,
+                 int B, int Hq, int Hkv, int L, int d, int block, int mode,
+                 void* workspace, size_t ws_bytes, void* stream);
+size_t bda_attn_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int block, int mode);
+
+/*
+ * Confidence commit ([LLaDA] SPRINT; [DGemma] Schedulers; [VLM-8B]).
+ * logits: [G, R, V] of dtype BDA_BF16 or BDA_F32 (G independent groups, e.g.
+ *   sequences; R canvas positions; V vocabulary).  Values must be finite.
+ * masked: [G, R] uint8, 1 = position still masked; updated in place.
+ * tokens: [G, R] int64; written only at the positions this call commits.
+ * For each group, among masked rows: c_r = largest softmax probability of
+ * the row (temperature 1) and a_r = its token (lowest id on ties).  Every row
+ * with c_r > threshold (strict, fp32) commits; if fewer than
+ * min(k_min, #masked) did, the masked rows with the largest c_r (lower row
+ * index first on ties) are added until that many have committed.  A commit
+ * sets tokens[g,r] = a_r and masked[g,r] = 0.  k_min >= 0.
+ * workspace: at least bda_commit_workspace_bytes(G, R, V) bytes of device
+ *   memory; no initial contents are required.
+ */
+int bda_commit(const void* logits, int dtype, int64_t* tokens, uint8_t* masked,
+               float threshold, int k_min, int G, int R, int V,
+               void* workspace, size_t ws_bytes, void* stream);
+size_t bda_commit_workspace_bytes(int G, int R, int V);
+
+/*
+ * Verify for linear speculative decoding ([NLD-3x] sec. 2).
+ * logits [B, R, V] (BDA_BF16 or BDA_F32), drafts [B, R] int64.
+ * argmax_out[B, R] int64 = lowest index of each row's largest logit;
+ * accept_len[B] int32 = first j with argmax != drafts[b, j], or R if none.
+ * workspace: at least bda_verify_workspace_bytes(B, R, V) bytes.
+ */
+int bda_verify(const void* logits, int dtype, const int64_t* drafts,
+               int64_t* argmax_out, int32_t* accept_len, int B, int R, int V,
+               void* workspace, size_t ws_bytes, void* stream);
+size_t bda_verify_workspace_bytes(int B, int R, int V);
+
+/*
+ * Host-only tile classifier (the rule the attention kernels use to skip and
+ * to take their unmasked fast path).  Rows [q0, q1) of the query tensor and
+ * keys [k0, k1) of the key tensor, in the row numbering of bda_attn_fwd for
+ * `mode` (HYBRID: L per half; DECODE/CAUSAL: n = block query rows, L keys).
+ * Returns BDA_TILE_FULL (every pair allowed), BDA_TILE_EMPTY (none) or
+ * BDA_TILE_PARTIAL; -1 on bad arguments.  Touches no device.
+ */
+int bda_classify_tile(int mode, int L, int block, int q0, int q1, int k0, int k1);
+
+/* Static description of an error code; never NULL. */
+const char* bda_strerror(int code);
+/* Detail of the calling thread's last failed call ("" if none). */
+const char* bda_last_error(void);
+/* Library version string. */
+const char* bda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BDA_H */

@@ -1,0 +1,110 @@
+"""Host-only checks of the C ABI: the library loads, exports what the header
+declares, rejects bad arguments before touching a device, and its tile
+classifier agrees with the oracle's dense-mask reduction."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import oracle
+import block_masked_attention_amd as bda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bda.h")
+
+# Distinct, 16-byte aligned, far-apart fake device addresses: every call below
+# fails validation before any HIP call, so nothing dereferences them.
+A, Bp, Cp, Dp, Wp = (ctypes.c_void_p(x << 32) for x in (1, 2, 3, 4, 5))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bda_\w+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(bda.lib, n), n
+
+
+def test_strings():
+    for code in range(5):
+        assert bda.lib.bda_strerror(code)
+    assert bda.lib.bda_strerror(99) == b"unknown error code"
+    assert bda.version().startswith("bda")
+
+
+def _attn(B=1, Hq=4, Hkv=2, L=64, d=128, block=8, mode=0, q=A, k=Bp, v=Cp, out=Dp, ws=None, nbytes=0):
+    return bda.lib.bda_attn_fwd(q, k, v, out, B, Hq, Hkv, L, d, block, mode, ws, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(out=None), 1), (dict(Hq=3, Hkv=2), 1), (dict(d=96), 2), (dict(d=256), 2),
+    (dict(block=0), 1), (dict(block=65), 1), (dict(mode=3), 1), (dict(B=0), 1), (dict(L=0), 1),
+    (dict(q=ctypes.c_void_p((1 << 32) + 8)), 1),                      # misaligned
+    (dict(out=ctypes.c_void_p((1 << 32) + 4096)), 1),                 # out overlaps q
+    (dict(mode=1, L=4124, block=28, Hq=32, Hkv=8), 3),                # split workspace missing
+])
+def test_attn_validation(kw, code):
+    assert _attn(**kw) == code
+    assert bda.lib.bda_last_error()
+
+
+def test_attn_workspace_sizes():
+    assert bda.attn_workspace_bytes(4, 32, 8, 2048, 128, 32, "hybrid") == 0
+    need = bda.attn_workspace_bytes(32, 32, 8, 4124, 128, 28, "decode")
+    assert need > 0
+    assert _attn(mode=1, L=4124, block=28, Hq=32, Hkv=8, B=32, ws=Wp, nbytes=need - 1) == 3
+    assert bda.attn_workspace_bytes(1, 3, 2, 10, 128, 2, "hybrid") == 0     # invalid -> 0
+
+
+def test_commit_validation():
+    c = bda.lib.bda_commit
+    assert c(A, 0, Bp, Cp, 0.9, 1, 0, 5, 10, None, 0, None) == 0             # nothing to do
+    assert c(A, 2, Bp, Cp, 0.9, 1, 1, 5, 10, Wp, 1 << 20, None) == 1         # dtype
+    assert c(A, 0, Bp, Cp, float("nan"), 1, 1, 5, 10, Wp, 1 << 20, None) == 1
+    assert c(A, 0, Bp, Cp, 0.9, -1, 1, 5, 10, Wp, 1 << 20, None) == 1
+    assert c(A, 0, Bp, Cp, 0.9, 1, 1, 5, 0, Wp, 1 << 20, None) == 1          # V
+    assert c(None, 0, Bp, Cp, 0.9, 1, 1, 5, 10, Wp, 1 << 20, None) == 1
+    assert c(A, 0, None, Cp, 0.9, 1, 1, 5, 10, Wp, 1 << 20, None) == 1
+    assert c(A, 0, Bp, Cp, 0.9, 1, 1, 5, 10, None, 0, None) == 3             # workspace
+    need = bda.lib.bda_commit_workspace_bytes(1, 5, 10)
+    assert c(A, 0, Bp, Cp, 0.9, 1, 1, 5, 10, Wp, need - 1, None) == 3
+    assert c(A, 0, ctypes.c_void_p((1 << 32) + 16), Cp, 0.9, 1, 1, 5, 10, Wp, need, None) == 1  # overlap
+
+
+def test_verify_validation():
+    f = bda.lib.bda_verify
+    assert f(A, 0, Bp, Cp, Dp, 0, 28, 100, None, 0, None) == 0
+    assert f(A, 0, Bp, Cp, None, 2, 28, 100, Wp, 1 << 20, None) == 1
+    assert f(A, 7, Bp, Cp, Dp, 2, 28, 100, Wp, 1 << 20, None) == 1
+    assert f(A, 0, Bp, Cp, Dp, 2, 28, 100, None, 0, None) == 3
+
+
+def _sweep():
+    for L in (1, 5, 16, 37, 64):
+        for b in sorted({1, 2, 3, 4, 7, 16, 32, L} & set(range(1, L + 1))):
+            yield "hybrid", L, b
+    for L, n in ((1, 1), (40, 7), (64, 28), (64, 64), (97, 33)):
+        yield "decode", L, n
+        yield "causal", L, n
+
+
+@pytest.mark.parametrize("mode,L,b", list(_sweep()))
+def test_classifier_matches_dense_mask(mode, L, b):
+    M = oracle.mask(mode, L, b)
+    rows, keys = M.shape
+    for tq in (1, 3, 8, 32):
+        for tk in (1, 5, 32, 64):
+            for q0 in range(0, rows, tq):
+                for k0 in range(0, keys, tk):
+                    q1, k1 = min(rows, q0 + tq), min(keys, k0 + tk)
+                    assert bda.classify_tile(mode, L, b, q0, q1, k0, k1) == oracle.tile_class(M, q0, q1, k0, k1), \
+                        (mode, L, b, q0, q1, k0, k1)
+    assert bda.classify_tile(mode, L, b, 0, rows + 1, 0, 1) == -1
+    assert bda.classify_tile(mode, L, b, 0, 1, 2, 1) == -1
