@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-diffusion hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu]
+
+Headline step: one training-form hybrid attention forward over [x_t ; x_0]
+(B=4, L=2048 per half, block 32, Hq=32, Hkv=8, d=128, bf16, synthetic
+N(0,1) inputs resident in HBM).  `value` = unmasked TFLOP/s, counting
+4*d FLOPs per allowed (query, key) pair per query head.
+
+Secondary lines (same JSON object): decode-form and verify-form attention,
+the confidence commit (committed tokens/s and HBM GB/s) and verify, each
+timed per launch with HIP events on the stream the kernels run on, with
+rotated input buffers for the HBM-bound ones so that the 256 MB last-level
+cache cannot serve repeated reads.
+
+`--copy-calibration` runs only a plain device copy of known size (for
+scaling rocprofv3 FETCH_SIZE/WRITE_SIZE counters to bytes).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0
+METRIC = "block-diffusion attn TFLOP/s (unmasked) & %MFMA peak; commit tokens/s & %HBM peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def hybrid_pairs(L, b):
+    """Allowed (query, key) pairs of one head of the training form (closed form)."""
+    tot = 0
+    for s in range(0, L, b):
+        n = min(b, L - s)
+        tot += n * (s + n)
+    return 2 * tot
+
+
+def decode_pairs(L, n):
+    return n * L
+
+
+def causal_pairs(L, n):
+    return n * (L - n) + n * (n + 1) // 2
+
+
+def time_launches(fn, iters, warmup, pre=None):
+    """Mean and median per-launch ms of fn(i) with HIP events on the current stream."""
+    import torch
+    for i in range(warmup):
+        if pre:
+            pre(i)
+        fn(i)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    for i in range(iters):
+        if pre:
+            pre(i)
+        starts[i].record()
+        fn(i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    return sum(ms) / len(ms), ms[len(ms) // 2]
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    x = torch.empty(n, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    x.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": n, "launches": 5}))
+
+
+def cpu_baseline_attention(case, budget_s=20.0):
+    """The oracle, untuned, on a bounded sample of the same workload: every
+    row of the query heads of the first kv head(s) of batch 0, the number of
+    kv heads doubled until one call takes about a quarter of budget_s."""
+    import oracle
+    L, blk = case.L, case.block
+    rows = 2 * L
+    pairs_per_head = hybrid_pairs(L, blk)
+    d = case.q.shape[-1]
+    G = case.q.shape[1] // case.k.shape[1]
+    Hkv, B = case.k.shape[1], case.q.shape[0]
+    kvh, nb = 1, 1
+    while True:
+        heads = G * kvh
+        t0 = time.perf_counter()
+        oracle.attention("hybrid", case.q[:nb, :heads], case.k[:nb, :kvh], case.v[:nb, :kvh], L, blk)
+        dt = time.perf_counter() - t0
+        flops = 4 * d * pairs_per_head * heads * nb
+        if dt > budget_s / 4 or (kvh == Hkv and nb == B):
+            break
+        if kvh < Hkv:
+            kvh = min(Hkv, kvh * 2)
+        else:
+            nb = min(B, nb * 2)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"all {rows} rows of {heads} query heads ({kvh} kv heads) of {nb} batch(es) "
+                      f"({flops / 1e9:.1f} GFLOP, {dt:.1f} s)"}
+
+
+def cpu_baseline_commit(logits, masked, tau, k_min):
+    import numpy as np
+    import oracle
+    G = logits.shape[0]
+    g = G                                   # the whole commit call is well under a minute of CPU work
+    tokens = np.full((g, logits.shape[1]), -1, dtype=np.int64)
+    t0 = time.perf_counter()
+    _, m, _ = oracle.commit(logits[:g], masked[:g].numpy(), tokens, tau, k_min)
+    dt = time.perf_counter() - t0
+    committed = int(masked[:g].numpy().sum() - m.sum())
+    return {"value": committed / dt, "unit": "committed tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"{g} of {G} groups ({committed} tokens, {dt:.2f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the multi-GPU "
+              "sharding of the path is a design note, not a measured configuration.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    import block_masked_attention_amd as bda
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---------------- headline: training-form hybrid attention
+    case = synth.hybrid_train()
+    B, Hq, S2, d = case.q.shape
+    Hkv, L, blk = case.k.shape[1], case.L, case.block
+    flops = 4 * d * hybrid_pairs(L, blk) * B * Hq
+    q, k, v = case.q.to(dev), case.k.to(dev), case.v.to(dev)
+    out = torch.empty_like(q)
+    log(f"[bench] training form: {flops / 1e9:.1f} GFLOP unmasked per step")
+    for _ in range(args.warmup):
+        bda.attn_fwd(q, k, v, "hybrid", blk, out=out)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        bda.attn_fwd(q, k, v, "hybrid", blk, out=out)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] training form: {ms * 1e3:.1f} us/step, {tflops:.1f} TFLOP/s "
+        f"({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 MFMA peak)")
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "attn_hybrid_B4_L2048_b32_traffic.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_sha") == _kernel_sha():
+            traffic = tr.get("bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "training-form block-diffusion attention over [x_t;x_0]",
+                   "B": B, "L": L, "seq_2L": S2, "block": blk, "Hq": Hq, "Hkv": Hkv, "head_dim": d,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+    }
+    del q, k, v, out
+
+    if not args.no_secondary:
+        result["secondary"] = secondary(bda, synth, torch, dev, args)
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle on a sample of the training form")
+        result["cpu_baseline"] = cpu_baseline_attention(case)
+        log(f"[bench] cpu baseline: {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+
+
+def _kernel_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("attn.hip", "common.h", "geometry.h"):
+        with open(os.path.join(ROOT, "block_masked_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def secondary(bda, synth, torch, dev, args):
+    res = {}
+    iters = max(20, args.steps)
+    # ---- decode-form attention (B=32, 28 queries over 4096 + 28 keys)
+    for name, maker, pairs in (("decode_attention", synth.decode_block, decode_pairs),
+                               ("verify_attention", synth.verify_block, causal_pairs)):
+        case = maker()
+        B, Hq, n, d = case.q.shape
+        L = case.L
+        fl = 4 * d * pairs(L, n) * B * Hq
+        sets = [(case.q.to(dev), case.k.to(dev), case.v.to(dev))]
+        g = torch.Generator(device=dev).manual_seed(1)
+        for _ in range(2):     # two more K/V sets so repeated launches stream from HBM
+            sets.append((sets[0][0], torch.randn(case.k.shape, generator=g, device=dev).to(torch.bfloat16),
+                         torch.randn(case.v.shape, generator=g, device=dev).to(torch.bfloat16)))
+        out = torch.empty_like(sets[0][0])
+        ws = torch.empty(max(1, bda.attn_workspace_bytes(B, Hq, case.k.shape[1], L, d, n, case.mode)),
+                         dtype=torch.uint8, device=dev)
+        mean, med = time_launches(lambda i: bda.attn_fwd(*sets[i % 3], case.mode, n, out=out, workspace=ws),
+                                  iters, 5)
+        byts = (case.q.numel() * 2 * 2) + case.k.numel() * 2 * 2
+        res[name] = {"B": B, "n": n, "kv_len": L, "us_per_call": round(mean * 1e3, 2),
+                     "TFLOP/s": round(fl / (mean * 1e-3) / 1e12, 2),
+                     "mfma_frac": round(fl / (mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "GB/s": round(byts / (mean * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(byts / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "algorithmic_bytes": byts}
+        log(f"[bench] {name}: {res[name]}")
+        del sets, out, ws
+        torch.cuda.empty_cache()
+
+    # ---- commit on decode-form logits [32, 28, 131072] bf16, threshold 0.85
+    logits, idx, masked0 = synth.commit_logits()
+    G, R, V = logits.shape
+    sets = [logits.to(dev)]
+    for j in range(2):
+        sets.append(sets[0].roll(shifts=j + 1, dims=0).contiguous())
+    tokens = torch.full((G, R), -1, dtype=torch.int64, device=dev)
+    masked = masked0.to(dev)
+    ws = torch.empty(bda.lib.bda_commit_workspace_bytes(G, R, V), dtype=torch.uint8, device=dev)
+    committed = []
+
+    def pre(i):
+        masked.fill_(1)
+
+    def run(i):
+        bda.commit(sets[i % 3], tokens, masked, 0.85, 1, workspace=ws)
+
+    mean, med = time_launches(run, iters, 5, pre=pre)
+    torch.cuda.synchronize()
+    n_commit = int(G * R - masked.sum().item())
+    byts = G * R * V * 2
+    res["commit"] = {"G": G, "R": R, "V": V, "threshold": 0.85, "k_min": 1,
+                     "us_per_call": round(mean * 1e3, 2), "committed_per_call": n_commit,
+                     "committed_tokens_per_s": round(n_commit / (mean * 1e-3), 1),
+                     "GB/s": round(byts / (mean * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(byts / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "algorithmic_bytes": byts}
+    log(f"[bench] commit: {res['commit']}")
+    if not args.no_cpu:
+        res["commit"]["cpu_baseline"] = cpu_baseline_commit(logits, masked0, 0.85, 1)
+
+    # ---- verify on [16, 28, 131072] bf16
+    vl, vidx, _ = synth.commit_logits(seed=6, G=16, R=28)
+    drafts, _ = synth.verify_drafts(vidx)
+    vsets = [vl.to(dev)] + [vl.to(dev).roll(shifts=j + 1, dims=0).contiguous() for j in range(2)]
+    dr = drafts.to(dev)
+    mean, med = time_launches(lambda i: bda.verify(vsets[i % 3], dr), iters, 5)
+    byts = vl.numel() * 2
+    res["verify"] = {"B": 16, "R": 28, "V": V, "us_per_call": round(mean * 1e3, 2),
+                     "GB/s": round(byts / (mean * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(byts / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "algorithmic_bytes": byts}
+    log(f"[bench] verify: {res['verify']}")
+    return res
+
+
+if __name__ == "__main__":
+    main()
