@@ -14,11 +14,11 @@
 // of a row are adjacent slots, so one staged K/V tile feeds all of them).
 //   S^T = K Q^T   v_mfma_f32_32x32x16_bf16, A = K tile (LDS), B = Q (registers)
 //   online softmax in the log2 domain on the S^T accumulator (lane = query)
-//   O^T += V^T P^T  same MFMA, A = V^T tile (LDS), B = P straight from the
-//                  S^T accumulator registers (no shuffle)
-// V is staged transposed, with the keys of every 16-key group permuted
-// (bits 2 and 3 of the key index swapped) so that each lane's eight P values
-// and its eight V^T values name the same keys.
+//   O^T += V^T P^T  same MFMA, A = V^T read with the LDS transpose read
+//                  (ds_read_b64_tr_b16) from the row-major V tile, B = P
+//                  straight from the S^T accumulator registers: the two
+//                  4-key transpose reads of a lane pick exactly the keys its
+//                  eight P values belong to, so nothing is shuffled.
 #include "common.h"
 #include "geometry.h"
 #include "internal.h"
@@ -26,15 +26,6 @@
 namespace bda {
 
 constexpr int kBN = 64;   // keys per staged tile (two 32-key MFMA subtiles)
-
-template <int D>
-struct Lds {
-  static constexpr int KP = D + 8;      // K tile row pitch (elements), +16 B pad
-  static constexpr int VP = kBN + 8;    // V^T tile row pitch (elements)
-  static constexpr int KE = kBN * KP;
-  static constexpr int VE = D * VP;
-  static constexpr int STAGE = KE + VE;
-};
 
 struct AttnArgs {
   const uint16_t* q;
@@ -52,17 +43,37 @@ __device__ __forceinline__ bool in_span(const Span& s, int j) {
   return (unsigned)(j - s.lo) < (unsigned)(s.hi - s.lo);
 }
 
+// LDS tiles are row-major (one key per row, d fastest, no padding) with the
+// 16-byte chunks of every row XOR-permuted by swz(row): a wavefront's K reads
+// (8 rows, one chunk column) and its V transpose reads (4 rows x 2 chunks per
+// 16 lanes) then touch all 32 banks exactly once.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+template <int D>
+__device__ __forceinline__ int chunk_off(int r, int c) {  // element offset of chunk c of row r
+  constexpr int CPR = D / 8;
+  return r * D + 8 * (c ^ (swz(r) & (CPR - 1)));
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane j receives element
+// (j & 3) of the 4-element row read by lane 4*e + (j >> 2), for e = 0..3.
+__device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) {
   constexpr int NT = NW * 64;
   constexpr int KSTEPS = D / 16;              // MFMA k-steps of Q K^T
   constexpr int DT = D / 32;                  // 32-row tiles of O^T
-  constexpr int KCH = kBN * D / 8;            // 16-byte chunks of a K tile
-  constexpr int KU = (KCH + NT - 1) / NT;
-  constexpr int VUN = (D / 2) * (kBN / 8);    // (d pair, 8-key octet) units of a V tile
-  constexpr int VU = (VUN + NT - 1) / NT;
-  using S = Lds<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * S::STAGE];
+  constexpr int CPR = D / 8;                  // 16-byte chunks per key row
+  constexpr int TCH = kBN * CPR;              // chunks of one K (or V) tile
+  constexpr int CU = (TCH + NT - 1) / NT;     // chunks per thread per tile
+  constexpr int TE = kBN * D;                 // elements of one K (or V) tile
+  constexpr int STAGE = 2 * TE;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[3 * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -93,46 +104,50 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
   const int g = pair - b * a.Hkv;
 
   // ---- my query slot
-  int qrow = 0, head = 0, rloc = 0;
+  int qrow = 0, head = 0;
   bool valid;
   if (a.mode == kHybrid) {
     const int per_half = NW / 2;
     const int half = w / per_half;
     const int s = (w - half * per_half) * 32 + ql;
-    rloc = s / a.G;
-    const int hh = s - rloc * a.G;
+    const int rloc = s / a.G;
     const int pos = qt * a.rows_per_wg + rloc;
     valid = rloc < a.rows_per_wg && pos < a.L;
     qrow = half * a.L + pos;
-    head = g * a.G + hh;
+    head = g * a.G + (s - rloc * a.G);
   } else {
     const int s = w * 32 + ql;
-    rloc = s / a.G;
-    const int hh = s - rloc * a.G;
+    const int rloc = s / a.G;
     const int r = qt * a.rows_per_wg + rloc;
     valid = rloc < a.rows_per_wg && r < a.n;
     qrow = r;
-    head = g * a.G + hh;
+    head = g * a.G + (s - rloc * a.G);
   }
   Span A{0, 0}, C{0, 0};
   if (valid) row_spans(a.mode, a.L, a.n, a.blk, qrow, A, C);
 
-  // ---- key ranges this workgroup walks (hull of its rows' spans)
-  Span U1{0, 0}, U2{0, 0};
+  // ---- key ranges: F is walked by the pipelined loop (every row of the
+  // workgroup may see every key of it); R1 and R2 are the remaining keys the
+  // rows need, walked tile by tile with per-wavefront classification.
+  Span F{0, 0}, R1{0, 0}, R2{0, 0};
   if (a.mode == kHybrid) {
     const int p0 = qt * a.rows_per_wg;
     const int p1 = imin(a.L, p0 + a.rows_per_wg);
     const int e = imin(a.L, ((p1 - 1) / a.blk + 1) * a.blk);
-    U1 = Span{(p0 / a.blk) * a.blk, e};     // x_t blocks of these rows
-    U2 = Span{a.L, a.L + e};                // x_0 prefix they need
+    const int s_min = (p0 / a.blk) * a.blk;     // clean prefix every row of the workgroup sees
+    F = Span{a.L, a.L + (s_min / kBN) * kBN};
+    R1 = Span{F.hi, a.L + e};                   // rest of the clean prefix / own clean blocks
+    R2 = Span{s_min, e};                        // noisy blocks of these rows
   } else {
-    const int r1 = imin(a.n, (qt + 1) * a.rows_per_wg);
-    const int hi = a.mode == kDecode ? a.L : a.L - a.n + r1;
-    U1 = Span{imax(0, split * a.split_keys), imin(hi, (split + 1) * a.split_keys)};
+    const int r0 = qt * a.rows_per_wg;
+    const int r1 = imin(a.n, r0 + a.rows_per_wg);
+    const int lo = split * a.split_keys;
+    const int hi = imin(a.mode == kDecode ? a.L : a.L - a.n + r1, lo + a.split_keys);
+    const int full_hi = imin(hi, a.mode == kDecode ? a.L : a.L - a.n + r0 + 1);
+    const int nfull = full_hi > lo ? (full_hi - lo) / kBN : 0;
+    F = Span{lo, lo + nfull * kBN};
+    R1 = Span{F.hi, imax(F.hi, hi)};
   }
-  const int n1 = U1.hi > U1.lo ? (U1.hi - U1.lo + kBN - 1) / kBN : 0;
-  const int n2 = U2.hi > U2.lo ? (U2.hi - U2.lo + kBN - 1) / kBN : 0;
-  const int nt = n1 + n2;
 
   // ---- Q operand in registers: lane (ql, hb) holds d = 16*ks + 8*hb + 0..7
   bf16x8 qreg[KSTEPS];
@@ -149,187 +164,218 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
   const uint16_t* kbase = a.k + kvoff;
   const uint16_t* vbase = a.v + kvoff;
 
-  u32x4 kreg[KU];
-  unsigned vreg[VU][8];
-
-  auto tile_range = [&](int i, int& t0, int& t1) {
-    if (i < n1) {
-      t0 = U1.lo + i * kBN;
-      t1 = imin(U1.hi, t0 + kBN);
-    } else {
-      t0 = U2.lo + (i - n1) * kBN;
-      t1 = imin(U2.hi, t0 + kBN);
+  // lane-constant LDS offsets (elements, within a stage)
+  const int k_row = ql * D;
+  const int k_swz = swz(ql) & (CPR - 1);
+  int v_off[DT];
+  {
+    const int j = lane & 15, gi = lane >> 4;
+    const int r = 4 * hb + (j >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int dcol = 32 * dt + 16 * (gi & 1) + 4 * (j & 3);
+      v_off[dt] = r * D + 8 * ((dcol >> 3) ^ (swz(r) & (CPR - 1))) + (dcol & 7);
     }
-  };
-  // Global -> registers.  Key rows at or past t1 are zero-filled so that no
-  // stale LDS bits (possibly NaN) meet a zero softmax weight.
+  }
+
+  u32x4 kreg[CU], vreg[CU];
+  // global -> registers for the tile starting at key t0 (rows past t1 repeat
+  // row t1-1: finite data that the masks below never let through)
   auto gload = [&](int t0, int t1) {
 #pragma unroll
-    for (int j = 0; j < KU; ++j) {
-      const int c = tid + j * NT;
-      const int row = c / (D / 8), col = c % (D / 8);
-      const bool ok = c < KCH && t0 + row < t1;
-      kreg[j] = ok ? *(const u32x4*)(kbase + (size_t)(t0 + row) * D + col * 8) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int j = 0; j < VU; ++j) {
-      const int u = tid + j * NT;
-      const int dp = u % (D / 2), oct = u / (D / 2);
-      const int k0 = 16 * (oct >> 1) + 4 * (oct & 1);   // keys k0..k0+3, k0+8..k0+11
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = t0 + k0 + (e & 3) + 8 * (e >> 2);
-        const bool ok = u < VUN && key < t1;
-        vreg[j][e] = ok ? *(const unsigned*)(vbase + (size_t)key * D + 2 * dp) : 0u;
+    for (int j = 0; j < CU; ++j) {
+      const int ch = tid + j * NT;
+      if (TCH % NT == 0 || ch < TCH) {
+        const int r = ch / CPR, c = ch % CPR;
+        const size_t off = (size_t)imin(t0 + r, t1 - 1) * D + 8 * c;
+        kreg[j] = *(const u32x4*)(kbase + off);
+        vreg[j] = *(const u32x4*)(vbase + off);
       }
     }
   };
-  // Registers -> LDS stage: K row-major (padded), V transposed (d-major) with
-  // the 8 keys of an octet landing on 8 consecutive permuted positions.
   auto lstore = [&](uint16_t* st) {
 #pragma unroll
-    for (int j = 0; j < KU; ++j) {
-      const int c = tid + j * NT;
-      if (c < KCH) {
-        const int row = c / (D / 8), col = c % (D / 8);
-        *(u32x4*)(st + row * S::KP + col * 8) = kreg[j];
-      }
-    }
-    uint16_t* vt = st + S::KE;
-#pragma unroll
-    for (int j = 0; j < VU; ++j) {
-      const int u = tid + j * NT;
-      if (u < VUN) {
-        const int dp = u % (D / 2), oct = u / (D / 2);
-        u32x4 lo, hi;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const unsigned x0 = vreg[j][2 * e], x1 = vreg[j][2 * e + 1];
-          lo[e] = (x0 & 0xffffu) | (x1 << 16);
-          hi[e] = (x0 >> 16) | (x1 & 0xffff0000u);
-        }
-        *(u32x4*)(vt + (2 * dp) * S::VP + 8 * oct) = lo;
-        *(u32x4*)(vt + (2 * dp + 1) * S::VP + 8 * oct) = hi;
+    for (int j = 0; j < CU; ++j) {
+      const int ch = tid + j * NT;
+      if (TCH % NT == 0 || ch < TCH) {
+        const int off = chunk_off<D>(ch / CPR, ch % CPR);
+        *(u32x4*)(st + off) = kreg[j];
+        *(u32x4*)(st + TE + off) = vreg[j];
       }
     }
   };
-
+  // S^T = K Q^T for one 32-key subtile of the stage
+  auto qk_sub = [&](const uint16_t* st, int sub, f32x16& s) {
+    s = f32x16{};
+    const uint16_t* kr = st + 32 * sub * D + k_row;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const bf16x8 kop = *(const bf16x8*)(kr + 8 * ((2 * ks + hb) ^ k_swz));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[ks], s, 0, 0, 0);
+    }
+  };
   f32x16 o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
-  const float sl2 = a.sl2;
-
-  if (nt > 0) {
-    int t0, t1;
-    tile_range(0, t0, t1);
-    gload(t0, t1);
-    lstore(smem);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < nt; ++it) {
-    int t0, t1;
-    tile_range(it, t0, t1);
-    if (it + 1 < nt) {
-      int u0, u1;
-      tile_range(it + 1, u0, u1);
-      gload(u0, u1);
+  // O^T += V^T P^T for one 16-key group kg (0..3) of the stage
+  auto pv_group = [&](const uint16_t* st, int kg, const bf16x8& pb) {
+    const uint16_t* vt = st + TE + 16 * kg * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const s16x4 lo = lds_read_tr(vt + v_off[dt]);
+      const s16x4 hi = lds_read_tr(vt + 8 * D + v_off[dt]);
+      typedef short s16x8 __attribute__((ext_vector_type(8)));
+      const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pb, o[dt], 0, 0, 0);
     }
-    const uint16_t* Ks = smem + (it & 1) * S::STAGE;
-    const uint16_t* Vt = Ks + S::KE;
+  };
 
-    // classify the two 32-key subtiles for this wavefront
-    int cls[2];
+  const float sl2 = a.sl2;
+  const float thr = 8.f / sl2;   // keep the running max until scores exceed it by 2^8 in weight
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // Online softmax of a tile's scores (lane = query; 16 keys per subtile).
+  // The running max only moves when some score exceeds it by more than thr,
+  // so the rescale of O is rare; the result is the same softmax.
+  auto softmax = [&](f32x16 (&s)[2], const bool (&act)[2], bf16x8 (&pb)[2][2]) -> float {
+    float mt = -INFINITY;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-      const int e0 = t0 + 32 * sub, e1 = imin(t1, e0 + 32);
-      if (e0 >= e1) {
-        cls[sub] = kEmpty;
-      } else {
-        const int c = inside(A, e0, e1) + inside(C, e0, e1);
-        const bool full = !valid || (e1 - e0 == 32 && c == 32);
-        const bool empty = !valid || c == 0;
-        cls[sub] = __all(empty) ? kEmpty : (__all(full) ? kFull : kPartial);
+      if (!act[sub]) continue;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[sub][i]);
+    }
+    mt = half_max(mt);
+    const bool grow = mt > m_run + thr;
+    const float m_use = grow ? mt : m_run;
+    const float alpha = grow ? exp2f((m_run - m_use) * sl2) : 1.f;
+    const float nb = m_use == -INFINITY ? 0.f : -m_use * sl2;
+    float ls = 0.f;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      if (!act[sub]) continue;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = exp2f(fmaf(s[sub][8 * kk + 2 * e], sl2, nb));
+          const float p1 = exp2f(fmaf(s[sub][8 * kk + 2 * e + 1], sl2, nb));
+          ls += p0 + p1;
+          pk[e] = pack_bf16x2(p0, p1);
+        }
+        pb[sub][kk] = __builtin_bit_cast(bf16x8, pk);
       }
     }
-
-    if (cls[0] != kEmpty || cls[1] != kEmpty) {
-      f32x16 s[2];
+    l_run = l_run * alpha + ls;
+    m_run = m_use;
+    return alpha;
+  };
+  auto rescale = [&](float alpha) {
+    if (__any(alpha != 1.f)) {
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        s[sub] = f32x16{};
-        if (cls[sub] == kEmpty) continue;
-        const uint16_t* kr = Ks + (32 * sub + ql) * S::KP + 8 * hb;
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-          const bf16x8 kop = *(const bf16x8*)(kr + 16 * ks);
-          s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[ks], s[sub], 0, 0, 0);
-        }
-        if (cls[sub] == kPartial) {
-          const int e1 = imin(t1, t0 + 32 * sub + 32);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int j = t0 + 32 * sub + 8 * (i >> 2) + 4 * hb + (i & 3);
-            const bool ok = j < e1 && (in_span(A, j) || in_span(C, j));
-            s[sub][i] = ok ? s[sub][i] : -INFINITY;
-          }
-        }
-      }
-      // online softmax (each lane: one query, 16 of the 32 keys per subtile)
-      float mt = -INFINITY;
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        if (cls[sub] == kEmpty) continue;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[sub][i]);
-      }
-      mt = half_max(mt);
-      const float m_new = fmaxf(m_run, mt);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f((m_run - m_use) * sl2);
-      const float nb = -m_use * sl2;
-      float ls = 0.f;
-      bf16x8 pb[2][2];
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        if (cls[sub] == kEmpty) continue;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          u32x4 pk;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p0 = exp2f(fmaf(s[sub][8 * kk + 2 * e], sl2, nb));
-            const float p1 = exp2f(fmaf(s[sub][8 * kk + 2 * e + 1], sl2, nb));
-            ls += p0 + p1;
-            pk[e] = pack_bf16x2(p0, p1);
-          }
-          pb[sub][kk] = __builtin_bit_cast(bf16x8, pk);
-        }
-      }
-      l_run = l_run * alpha + ls;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-      }
-      m_run = m_new;
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        if (cls[sub] == kEmpty) continue;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const uint16_t* vr = Vt + ql * S::VP + 16 * (2 * sub + kk) + 8 * hb;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const bf16x8 vop = *(const bf16x8*)(vr + 32 * dt * S::VP);
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[sub][kk], o[dt], 0, 0, 0);
-          }
-        }
-      }
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
     }
+  };
 
-    if (it + 1 < nt) lstore(smem + ((it + 1) & 1) * S::STAGE);
+  // ---- pipelined walk over F: stage i%3 holds tile i; while the softmax of
+  // tile i runs, the MFMAs of tile i+1's scores are in flight; tile i+2 is
+  // stored and tile i+3 fetched during tile i's P V.
+  const int nf = (F.hi - F.lo) / kBN;
+  if (nf > 0) {
+    const bool act[2] = {true, true};
+    gload(F.lo, F.lo + kBN);
+    lstore(smem);
+    if (nf > 1) {
+      gload(F.lo + kBN, F.lo + 2 * kBN);
+      lstore(smem + STAGE);
+    }
+    if (nf > 2) gload(F.lo + 2 * kBN, F.lo + 3 * kBN);
     __syncthreads();
+    f32x16 s[2];
+    qk_sub(smem, 0, s[0]);
+    qk_sub(smem, 1, s[1]);
+    int st = 0;
+    for (int i = 0; i + 1 < nf; ++i) {
+      const int stn = st == 2 ? 0 : st + 1;
+      const int stp = stn == 2 ? 0 : stn + 1;
+      f32x16 sn[2];
+      qk_sub(smem + stn * STAGE, 0, sn[0]);
+      qk_sub(smem + stn * STAGE, 1, sn[1]);
+      bf16x8 pb[2][2];
+      const float alpha = softmax(s, act, pb);
+      rescale(alpha);
+#pragma unroll
+      for (int kg = 0; kg < 4; ++kg) pv_group(smem + st * STAGE, kg, pb[kg >> 1][kg & 1]);
+      lstore(smem + stp * STAGE);
+      {
+        const int t = F.lo + imin(i + 3, nf - 1) * kBN;
+        gload(t, t + kBN);
+      }
+      __syncthreads();
+      s[0] = sn[0];
+      s[1] = sn[1];
+      st = stn;
+    }
+    bf16x8 pb[2][2];
+    const float alpha = softmax(s, act, pb);
+    rescale(alpha);
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) pv_group(smem + st * STAGE, kg, pb[kg >> 1][kg & 1]);
+    __syncthreads();
+  }
+
+  // ---- boundary tiles: per-wavefront FULL / EMPTY / PARTIAL classification
+#pragma unroll 1
+  for (int seg = 0; seg < 2; ++seg) {
+    const Span R = seg == 0 ? R1 : R2;
+#pragma unroll 1
+    for (int t0 = R.lo; t0 < R.hi; t0 += kBN) {
+      const int t1 = imin(R.hi, t0 + kBN);
+      gload(t0, t1);
+      lstore(smem);
+      __syncthreads();
+      bool act[2], part[2];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int e0 = t0 + 32 * sub, e1 = imin(t1, e0 + 32);
+        if (e0 >= e1) {
+          act[sub] = false;
+          part[sub] = false;
+        } else {
+          const int c = inside(A, e0, e1) + inside(C, e0, e1);
+          const bool full = !valid || (e1 - e0 == 32 && c == 32);
+          const bool empty = !valid || c == 0;
+          act[sub] = !__all(empty);
+          part[sub] = !__all(full);
+        }
+      }
+      if (act[0] || act[1]) {
+        f32x16 s[2];
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          if (!act[sub]) continue;
+          qk_sub(smem, sub, s[sub]);
+          if (part[sub]) {
+            const int e1 = imin(t1, t0 + 32 * sub + 32);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int j = t0 + 32 * sub + 8 * (i >> 2) + 4 * hb + (i & 3);
+              const bool ok = j < e1 && (in_span(A, j) || in_span(C, j));
+              s[sub][i] = ok ? s[sub][i] : -INFINITY;
+            }
+          }
+        }
+        bf16x8 pb[2][2];
+        const float alpha = softmax(s, act, pb);
+        rescale(alpha);
+#pragma unroll
+        for (int kg = 0; kg < 4; ++kg) {
+          if (act[kg >> 1]) pv_group(smem, kg, pb[kg >> 1][kg & 1]);
+        }
+      }
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: lane (ql, hb) holds d = 32*dt + 8*(i/4) + 4*hb + (i%4)
