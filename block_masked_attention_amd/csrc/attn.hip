@@ -248,7 +248,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
     mt = half_max(mt);
     const bool grow = mt > m_run + thr;
     const float m_use = grow ? mt : m_run;
-    const float alpha = grow ? exp2f((m_run - m_use) * sl2) : 1.f;
+    const float alpha = grow ? exp2_fast((m_run - m_use) * sl2) : 1.f;
     const float nb = m_use == -INFINITY ? 0.f : -m_use * sl2;
     float ls = 0.f;
 #pragma unroll
@@ -259,8 +259,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
         u32x4 pk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = exp2f(fmaf(s[sub][8 * kk + 2 * e], sl2, nb));
-          const float p1 = exp2f(fmaf(s[sub][8 * kk + 2 * e + 1], sl2, nb));
+          const float p0 = exp2_fast(fmaf(s[sub][8 * kk + 2 * e], sl2, nb));
+          const float p1 = exp2_fast(fmaf(s[sub][8 * kk + 2 * e + 1], sl2, nb));
           ls += p0 + p1;
           pk[e] = pack_bf16x2(p0, p1);
         }
@@ -432,7 +432,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   for (int s = 0; s < n_splits; ++s) {
     const float ms = part_ml[((size_t)s * rows + row) * 2];
     if (ms == -INFINITY) continue;
-    const float wgt = exp2f(ms - M);
+    const float wgt = exp2_fast(ms - M);
     l += wgt * part_ml[((size_t)s * rows + row) * 2 + 1];
     const f32x4 x = *(const f32x4*)(part_o + ((size_t)s * rows + row) * D + c);
     acc += wgt * x;

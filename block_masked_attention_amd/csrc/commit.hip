@@ -46,7 +46,7 @@ __device__ __forceinline__ Stat merge(Stat x, Stat y, bool with_z) {
     if (r.m == -INFINITY) {
       r.z = 0.f;
     } else {
-      r.z = x.z * exp2f((x.m - r.m) * kLog2e) + y.z * exp2f((y.m - r.m) * kLog2e);
+      r.z = x.z * exp2_fast((x.m - r.m) * kLog2e) + y.z * exp2_fast((y.m - r.m) * kLog2e);
     }
   } else {
     r.z = 0.f;
@@ -70,7 +70,7 @@ __device__ __forceinline__ void fold8(Stat& s, const float (&x)[8], int base) {
     int idx = 7;
 #pragma unroll
     for (int e = 6; e >= 0; --e) idx = x[e] == lm ? e : idx;
-    if (WITH_Z) s.z = s.m == -INFINITY ? 0.f : s.z * exp2f((s.m - lm) * kLog2e);
+    if (WITH_Z) s.z = s.m == -INFINITY ? 0.f : s.z * exp2_fast((s.m - lm) * kLog2e);
     s.m = lm;
     s.a = base + idx;
   }
@@ -78,7 +78,7 @@ __device__ __forceinline__ void fold8(Stat& s, const float (&x)[8], int base) {
     const float nb = -s.m * kLog2e;
     float acc = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc += exp2f(fmaf(x[e], kLog2e, nb));
+    for (int e = 0; e < 8; ++e) acc += exp2_fast(fmaf(x[e], kLog2e, nb));
     s.z += acc;
   }
 }

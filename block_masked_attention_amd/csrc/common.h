@@ -25,6 +25,11 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(unsigned, v);
 }
 
+// 2^x with the hardware v_exp_f32 alone.  exp2f() wraps it in range fixes for
+// results below 2^-126 (compare, two selects, add, ldexp); those results only
+// ever weigh against terms >= 1 here, so they are flushed to zero instead.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Values of the other half-wavefront (lanes l ^ 32): permlane32_swap(x, x)
 // returns {lower-half value, upper-half value} in every lane.
 __device__ __forceinline__ float half_sum(float x) {
