@@ -44,15 +44,25 @@ __device__ __forceinline__ bool in_span(const Span& s, int j) {
 }
 
 // LDS tiles are row-major (one key per row, d fastest, no padding) with the
-// 16-byte chunks of every row XOR-permuted by swz(row): a wavefront's K reads
-// (8 rows, one chunk column) and its V transpose reads (4 rows x 2 chunks per
-// 16 lanes) then touch all 32 banks exactly once.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// 16-byte chunks of every row XOR-permuted by swz<D>(row).  gfx950's LDS has
+// 64 four-byte banks (256 bytes per clock); the permutation puts the 16 rows
+// of a wavefront's K operand read (16 lanes per clock at 16 bytes) and the
+// 4 rows x 4 chunks of a transpose read (32 lanes per clock at 8 bytes) on
+// 16 distinct bank groups.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if (D >= 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  if (D == 64) {
+    const int x = (r >> 1) & 7;   // two 128-byte rows share a bank line
+    return ((x & 1) << 2) | ((x >> 1) & 3);
+  }
+  return r & 3;
+}
 
 template <int D>
 __device__ __forceinline__ int chunk_off(int r, int c) {  // element offset of chunk c of row r
   constexpr int CPR = D / 8;
-  return r * D + 8 * (c ^ (swz(r) & (CPR - 1)));
+  return r * D + 8 * (c ^ (swz<D>(r) & (CPR - 1)));
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -63,8 +73,12 @@ __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) {
+// One workgroup = NW wavefronts; a wavefront owns QPW query slots, handled as
+// QPW/32 MFMA column blocks that share every K and V operand read from LDS
+// (64 slots per wavefront halve the LDS traffic per FLOP of 32).
+template <int D, int NW, int QPW>
+__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
+  constexpr int NQB = QPW / 32;               // 32-query column blocks per wavefront
   constexpr int NT = NW * 64;
   constexpr int KSTEPS = D / 16;              // MFMA k-steps of Q K^T
   constexpr int DT = D / 32;                  // 32-row tiles of O^T
@@ -103,28 +117,33 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
   const int b = pair / a.Hkv;
   const int g = pair - b * a.Hkv;
 
-  // ---- my query slot
-  int qrow = 0, head = 0;
-  bool valid;
-  if (a.mode == kHybrid) {
-    const int per_half = NW / 2;
-    const int half = w / per_half;
-    const int s = (w - half * per_half) * 32 + ql;
-    const int rloc = s / a.G;
-    const int pos = qt * a.rows_per_wg + rloc;
-    valid = rloc < a.rows_per_wg && pos < a.L;
-    qrow = half * a.L + pos;
-    head = g * a.G + (s - rloc * a.G);
-  } else {
-    const int s = w * 32 + ql;
-    const int rloc = s / a.G;
-    const int r = qt * a.rows_per_wg + rloc;
-    valid = rloc < a.rows_per_wg && r < a.n;
-    qrow = r;
-    head = g * a.G + (s - rloc * a.G);
+  // ---- my query slots (one per column block)
+  int qrow[NQB], head[NQB];
+  bool valid[NQB];
+  Span A[NQB], C[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    if (a.mode == kHybrid) {
+      const int per_half = NW / 2;
+      const int half = w / per_half;
+      const int s = ((w - half * per_half) * NQB + qb) * 32 + ql;
+      const int rloc = s / a.G;
+      const int pos = qt * a.rows_per_wg + rloc;
+      valid[qb] = rloc < a.rows_per_wg && pos < a.L;
+      qrow[qb] = half * a.L + pos;
+      head[qb] = g * a.G + (s - rloc * a.G);
+    } else {
+      const int s = (w * NQB + qb) * 32 + ql;
+      const int rloc = s / a.G;
+      const int r = qt * a.rows_per_wg + rloc;
+      valid[qb] = rloc < a.rows_per_wg && r < a.n;
+      qrow[qb] = r;
+      head[qb] = g * a.G + (s - rloc * a.G);
+    }
+    A[qb] = Span{0, 0};
+    C[qb] = Span{0, 0};
+    if (valid[qb]) row_spans(a.mode, a.L, a.n, a.blk, qrow[qb], A[qb], C[qb]);
   }
-  Span A{0, 0}, C{0, 0};
-  if (valid) row_spans(a.mode, a.L, a.n, a.blk, qrow, A, C);
 
   // ---- key ranges: F is walked by the pipelined loop (every row of the
   // workgroup may see every key of it); R1 and R2 are the remaining keys the
@@ -149,14 +168,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
     R1 = Span{F.hi, imax(F.hi, hi)};
   }
 
-  // ---- Q operand in registers: lane (ql, hb) holds d = 16*ks + 8*hb + 0..7
-  bf16x8 qreg[KSTEPS];
-  {
-    const uint16_t* qp = a.q + ((size_t)(b * a.Hq + head) * a.Sq + qrow) * D + 8 * hb;
+  // ---- Q operands in registers: lane (ql, hb) holds d = 16*ks + 8*hb + 0..7
+  bf16x8 qreg[NQB][KSTEPS];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    const uint16_t* qp = a.q + ((size_t)(b * a.Hq + head[qb]) * a.Sq + qrow[qb]) * D + 8 * hb;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      u32x4 x = valid ? *(const u32x4*)(qp + 16 * ks) : u32x4{0, 0, 0, 0};
-      qreg[ks] = __builtin_bit_cast(bf16x8, x);
+      u32x4 x = valid[qb] ? *(const u32x4*)(qp + 16 * ks) : u32x4{0, 0, 0, 0};
+      qreg[qb][ks] = __builtin_bit_cast(bf16x8, x);
     }
   }
 
@@ -166,15 +186,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
 
   // lane-constant LDS offsets (elements, within a stage)
   const int k_row = ql * D;
-  const int k_swz = swz(ql) & (CPR - 1);
-  int v_off[DT];
+  const int k_swz = swz<D>(ql) & (CPR - 1);   // rows 32*sub + ql share it
+  int v_lo[DT], v_hi[DT];                       // keys 4*hb + j/4 and 8 further
   {
     const int j = lane & 15, gi = lane >> 4;
     const int r = 4 * hb + (j >> 2);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const int dcol = 32 * dt + 16 * (gi & 1) + 4 * (j & 3);
-      v_off[dt] = r * D + 8 * ((dcol >> 3) ^ (swz(r) & (CPR - 1))) + (dcol & 7);
+      v_lo[dt] = chunk_off<D>(r, dcol >> 3) + (dcol & 7);
+      v_hi[dt] = chunk_off<D>(r + 8, dcol >> 3) + (dcol & 7);
     }
   }
 
@@ -204,125 +225,138 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       }
     }
   };
-  // S^T = K Q^T for one 32-key subtile of the stage
-  auto qk_sub = [&](const uint16_t* st, int sub, f32x16& s) {
-    s = f32x16{};
+  // S^T = K Q^T for one 32-key subtile of a stage, all column blocks
+  auto qk_sub = [&](const uint16_t* st, int sub, f32x16 (&s)[NQB]) {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) s[qb] = f32x16{};
     const uint16_t* kr = st + 32 * sub * D + k_row;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       const bf16x8 kop = *(const bf16x8*)(kr + 8 * ((2 * ks + hb) ^ k_swz));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[ks], s, 0, 0, 0);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[qb][ks], s[qb], 0, 0, 0);
     }
   };
-  f32x16 o[DT];
+  f32x16 o[NQB][DT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
-  // O^T += V^T P^T for one 16-key group kg (0..3) of the stage
-  auto pv_group = [&](const uint16_t* st, int kg, const bf16x8& pb) {
-    const uint16_t* vt = st + TE + 16 * kg * D;
+  for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const s16x4 lo = lds_read_tr(vt + v_off[dt]);
-      const s16x4 hi = lds_read_tr(vt + 8 * D + v_off[dt]);
-      typedef short s16x8 __attribute__((ext_vector_type(8)));
-      const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pb, o[dt], 0, 0, 0);
+    for (int dt = 0; dt < DT; ++dt) o[qb][dt] = f32x16{};
+  // O^T += V^T P^T for one 32-key subtile (two 16-key MFMA k-steps)
+  auto pv_sub = [&](const uint16_t* st, int sub, const bf16x8 (&pb)[NQB][2]) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const uint16_t* vt = st + TE + 16 * (2 * sub + kk) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const s16x4 lo = lds_read_tr(vt + v_lo[dt]);
+        const s16x4 hi = lds_read_tr(vt + v_hi[dt]);
+        typedef short s16x8 __attribute__((ext_vector_type(8)));
+        const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+          o[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[qb][kk], o[qb][dt], 0, 0, 0);
+      }
     }
   };
 
   const float sl2 = a.sl2;
   const float thr = 8.f / sl2;   // keep the running max until scores exceed it by 2^8 in weight
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run[NQB], l_run[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+  }
 
-  // Online softmax of a tile's scores (lane = query; 16 keys per subtile).
-  // The running max only moves when some score exceeds it by more than thr,
-  // so the rescale of O is rare; the result is the same softmax.
-  auto softmax = [&](f32x16 (&s)[2], const bool (&act)[2], bf16x8 (&pb)[2][2]) -> float {
-    float mt = -INFINITY;
+  // Online softmax of one 32-key subtile (lane = query of each column block,
+  // 16 of the 32 keys).  The running max only moves when a score exceeds it
+  // by more than thr, so the rescale of O is rare; the result is the same
+  // softmax.  Returns through alpha the factor O must be scaled by.
+  auto softmax_sub = [&](const f32x16 (&s)[NQB], bf16x8 (&pb)[NQB][2], float (&alpha)[NQB]) {
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      if (!act[sub]) continue;
+    for (int qb = 0; qb < NQB; ++qb) {
+      float mt = s[qb][0];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[sub][i]);
-    }
-    mt = half_max(mt);
-    const bool grow = mt > m_run + thr;
-    const float m_use = grow ? mt : m_run;
-    const float alpha = grow ? exp2_fast((m_run - m_use) * sl2) : 1.f;
-    const float nb = m_use == -INFINITY ? 0.f : -m_use * sl2;
-    float ls = 0.f;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      if (!act[sub]) continue;
+      for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[qb][i]);
+      mt = half_max(mt);
+      const bool grow = mt > m_run[qb] + thr;
+      const float m_use = grow ? mt : m_run[qb];
+      alpha[qb] = grow ? exp2_fast((m_run[qb] - m_use) * sl2) : 1.f;
+      const float nb = m_use == -INFINITY ? 0.f : -m_use * sl2;
+      float ls = 0.f;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         u32x4 pk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = exp2_fast(fmaf(s[sub][8 * kk + 2 * e], sl2, nb));
-          const float p1 = exp2_fast(fmaf(s[sub][8 * kk + 2 * e + 1], sl2, nb));
+          const float p0 = exp2_fast(fmaf(s[qb][8 * kk + 2 * e], sl2, nb));
+          const float p1 = exp2_fast(fmaf(s[qb][8 * kk + 2 * e + 1], sl2, nb));
           ls += p0 + p1;
           pk[e] = pack_bf16x2(p0, p1);
         }
-        pb[sub][kk] = __builtin_bit_cast(bf16x8, pk);
+        pb[qb][kk] = __builtin_bit_cast(bf16x8, pk);
       }
+      l_run[qb] = l_run[qb] * alpha[qb] + ls;
+      m_run[qb] = m_use;
     }
-    l_run = l_run * alpha + ls;
-    m_run = m_use;
-    return alpha;
   };
-  auto rescale = [&](float alpha) {
-    if (__any(alpha != 1.f)) {
+  auto rescale = [&](const float (&alpha)[NQB]) {
+    bool any = false;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    for (int qb = 0; qb < NQB; ++qb) any |= alpha[qb] != 1.f;
+    if (__any(any)) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[qb][dt] *= alpha[qb];
     }
   };
 
-  // ---- pipelined walk over F: stage i%3 holds tile i; while the softmax of
-  // tile i runs, the MFMAs of tile i+1's scores are in flight; tile i+2 is
-  // stored and tile i+3 fetched during tile i's P V.
+  // ---- pipelined walk over F (stage t%3 holds tile t).  Per tile: the
+  // MFMAs of the next subtile's scores are issued together with the softmax
+  // of the current one; tile t+2 is stored and tile t+3 fetched during P V.
+  // The last iteration computes (and drops) scores of a duplicate tile, so
+  // the loop body has no branch besides the rare rescale.
   const int nf = (F.hi - F.lo) / kBN;
   if (nf > 0) {
-    const bool act[2] = {true, true};
     gload(F.lo, F.lo + kBN);
     lstore(smem);
-    if (nf > 1) {
-      gload(F.lo + kBN, F.lo + 2 * kBN);
+    {
+      const int t = F.lo + imin(1, nf - 1) * kBN;
+      gload(t, t + kBN);
       lstore(smem + STAGE);
+      const int t2 = F.lo + imin(2, nf - 1) * kBN;
+      gload(t2, t2 + kBN);
     }
-    if (nf > 2) gload(F.lo + 2 * kBN, F.lo + 3 * kBN);
     __syncthreads();
-    f32x16 s[2];
-    qk_sub(smem, 0, s[0]);
-    qk_sub(smem, 1, s[1]);
+    f32x16 sa[NQB], sb[NQB];
+    qk_sub(smem, 0, sa);
     int st = 0;
-    for (int i = 0; i + 1 < nf; ++i) {
+#pragma unroll 1
+    for (int i = 0; i < nf; ++i) {
       const int stn = st == 2 ? 0 : st + 1;
       const int stp = stn == 2 ? 0 : stn + 1;
-      f32x16 sn[2];
-      qk_sub(smem + stn * STAGE, 0, sn[0]);
-      qk_sub(smem + stn * STAGE, 1, sn[1]);
-      bf16x8 pb[2][2];
-      const float alpha = softmax(s, act, pb);
+      const uint16_t* cur = smem + st * STAGE;
+      bf16x8 pb[NQB][2];
+      float alpha[NQB];
+      qk_sub(cur, 1, sb);
+      softmax_sub(sa, pb, alpha);
       rescale(alpha);
-#pragma unroll
-      for (int kg = 0; kg < 4; ++kg) pv_group(smem + st * STAGE, kg, pb[kg >> 1][kg & 1]);
+      pv_sub(cur, 0, pb);
       lstore(smem + stp * STAGE);
+      qk_sub(smem + stn * STAGE, 0, sa);
+      softmax_sub(sb, pb, alpha);
+      rescale(alpha);
+      pv_sub(cur, 1, pb);
       {
         const int t = F.lo + imin(i + 3, nf - 1) * kBN;
         gload(t, t + kBN);
       }
       __syncthreads();
-      s[0] = sn[0];
-      s[1] = sn[1];
       st = stn;
     }
-    bf16x8 pb[2][2];
-    const float alpha = softmax(s, act, pb);
-    rescale(alpha);
-#pragma unroll
-    for (int kg = 0; kg < 4; ++kg) pv_group(smem + st * STAGE, kg, pb[kg >> 1][kg & 1]);
-    __syncthreads();
   }
 
   // ---- boundary tiles: per-wavefront FULL / EMPTY / PARTIAL classification
@@ -335,81 +369,76 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       gload(t0, t1);
       lstore(smem);
       __syncthreads();
-      bool act[2], part[2];
-#pragma unroll
+#pragma unroll 1
       for (int sub = 0; sub < 2; ++sub) {
         const int e0 = t0 + 32 * sub, e1 = imin(t1, e0 + 32);
-        if (e0 >= e1) {
-          act[sub] = false;
-          part[sub] = false;
-        } else {
-          const int c = inside(A, e0, e1) + inside(C, e0, e1);
-          const bool full = !valid || (e1 - e0 == 32 && c == 32);
-          const bool empty = !valid || c == 0;
-          act[sub] = !__all(empty);
-          part[sub] = !__all(full);
-        }
-      }
-      if (act[0] || act[1]) {
-        f32x16 s[2];
+        if (e0 >= e1) break;
+        bool full = true, empty = true;
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-          if (!act[sub]) continue;
-          qk_sub(smem, sub, s[sub]);
-          if (part[sub]) {
-            const int e1 = imin(t1, t0 + 32 * sub + 32);
+        for (int qb = 0; qb < NQB; ++qb) {
+          const int c = inside(A[qb], e0, e1) + inside(C[qb], e0, e1);
+          full &= !valid[qb] || (e1 - e0 == 32 && c == 32);
+          empty &= !valid[qb] || c == 0;
+        }
+        if (__all(empty)) continue;
+        f32x16 s[NQB];
+        qk_sub(smem, sub, s);
+        if (!__all(full)) {
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-              const int j = t0 + 32 * sub + 8 * (i >> 2) + 4 * hb + (i & 3);
-              const bool ok = j < e1 && (in_span(A, j) || in_span(C, j));
-              s[sub][i] = ok ? s[sub][i] : -INFINITY;
+              const int j = e0 + 8 * (i >> 2) + 4 * hb + (i & 3);
+              const bool ok = j < e1 && (in_span(A[qb], j) || in_span(C[qb], j));
+              s[qb][i] = ok ? s[qb][i] : -INFINITY;
             }
           }
         }
-        bf16x8 pb[2][2];
-        const float alpha = softmax(s, act, pb);
+        bf16x8 pb[NQB][2];
+        float alpha[NQB];
+        softmax_sub(s, pb, alpha);
         rescale(alpha);
-#pragma unroll
-        for (int kg = 0; kg < 4; ++kg) {
-          if (act[kg >> 1]) pv_group(smem, kg, pb[kg >> 1][kg & 1]);
-        }
+        pv_sub(smem, sub, pb);
       }
       __syncthreads();
     }
   }
 
   // ---- epilogue: lane (ql, hb) holds d = 32*dt + 8*(i/4) + 4*hb + (i%4)
-  const float l_tot = half_sum(l_run);
-  if (!valid) return;
-  if (a.n_splits == 1) {
-    const float inv = 1.f / l_tot;
-    uint16_t* op = a.out + ((size_t)(b * a.Hq + head) * a.Sq + qrow) * D + 4 * hb;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+  for (int qb = 0; qb < NQB; ++qb) {
+    const float l_tot = half_sum(l_run[qb]);
+    if (!valid[qb]) continue;
+    if (a.n_splits == 1) {
+      const float inv = 1.f / l_tot;
+      uint16_t* op = a.out + ((size_t)(b * a.Hq + head[qb]) * a.Sq + qrow[qb]) * D + 4 * hb;
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        u32x2 pk;
-        pk[0] = pack_bf16x2(o[dt][4 * i4] * inv, o[dt][4 * i4 + 1] * inv);
-        pk[1] = pack_bf16x2(o[dt][4 * i4 + 2] * inv, o[dt][4 * i4 + 3] * inv);
-        *(u32x2*)(op + 32 * dt + 8 * i4) = pk;
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          u32x2 pk;
+          pk[0] = pack_bf16x2(o[qb][dt][4 * i4] * inv, o[qb][dt][4 * i4 + 1] * inv);
+          pk[1] = pack_bf16x2(o[qb][dt][4 * i4 + 2] * inv, o[qb][dt][4 * i4 + 3] * inv);
+          *(u32x2*)(op + 32 * dt + 8 * i4) = pk;
+        }
       }
-    }
-  } else {
-    const size_t rows = (size_t)a.B * a.Hq * a.n;
-    const size_t row = (size_t)(b * a.Hq + head) * a.n + qrow;
-    float* po = a.part_o + ((size_t)split * rows + row) * D + 4 * hb;
+    } else {
+      const size_t rows = (size_t)a.B * a.Hq * a.n;
+      const size_t row = (size_t)(b * a.Hq + head[qb]) * a.n + qrow[qb];
+      float* po = a.part_o + ((size_t)split * rows + row) * D + 4 * hb;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+      for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        f32x4 x{o[dt][4 * i4], o[dt][4 * i4 + 1], o[dt][4 * i4 + 2], o[dt][4 * i4 + 3]};
-        *(f32x4*)(po + 32 * dt + 8 * i4) = x;
+        for (int i4 = 0; i4 < 4; ++i4) {
+          f32x4 x{o[qb][dt][4 * i4], o[qb][dt][4 * i4 + 1], o[qb][dt][4 * i4 + 2], o[qb][dt][4 * i4 + 3]};
+          *(f32x4*)(po + 32 * dt + 8 * i4) = x;
+        }
       }
-    }
-    if (hb == 0) {
-      float* pm = a.part_ml + ((size_t)split * rows + row) * 2;
-      pm[0] = m_run == -INFINITY ? -INFINITY : m_run * sl2;
-      pm[1] = l_tot;
+      if (hb == 0) {
+        float* pm = a.part_ml + ((size_t)split * rows + row) * 2;
+        pm[0] = m_run[qb] == -INFINITY ? -INFINITY : m_run[qb] * sl2;
+        pm[1] = l_tot;
+      }
     }
   }
 }
@@ -464,7 +493,8 @@ int attn_make_plan(int B, int Hq, int Hkv, int L, int d, int block, int mode, At
     x.n = 2 * L;
     x.Sq = x.Sk = 2 * L;
     x.nw = L >= 256 ? 8 : 4;
-    const int slots_half = (x.nw / 2) * 32;
+    x.qpw = 32;
+    const int slots_half = (x.nw / 2) * x.qpw;
     if (x.G > slots_half) {
       *why = "Hq/Hkv larger than the query slots of half a workgroup";
       return 2;
@@ -476,7 +506,8 @@ int attn_make_plan(int B, int Hq, int Hkv, int L, int d, int block, int mode, At
     x.Sq = block;
     x.Sk = L;
     x.nw = block >= 128 ? 8 : 4;
-    const int slots = x.nw * 32;
+    x.qpw = 32;
+    const int slots = x.nw * x.qpw;
     if (x.G > slots) {
       *why = "Hq/Hkv larger than the query slots of a workgroup";
       return 2;
@@ -511,15 +542,15 @@ int attn_make_plan(int B, int Hq, int Hkv, int L, int d, int block, int mode, At
   return 0;
 }
 
-template <int D, int NW>
+template <int D, int NW, int QPW>
 static hipError_t launch_main(const AttnArgs& a, long long grid, hipStream_t st) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, QPW>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a);
   return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_d(const AttnPlan& p, const AttnArgs& a, hipStream_t st) {
-  hipError_t e = p.nw == 8 ? launch_main<D, 8>(a, p.grid, st) : launch_main<D, 4>(a, p.grid, st);
+  hipError_t e = p.nw == 8 ? launch_main<D, 8, 32>(a, p.grid, st) : launch_main<D, 4, 32>(a, p.grid, st);
   if (e != hipSuccess || p.n_splits == 1) return e;
   const long long rows = (long long)p.B * p.Hq * p.n;
   const long long threads = rows * (D / 4);

@@ -12,7 +12,8 @@ namespace bda {
 struct AttnPlan {
   int mode, B, Hq, Hkv, G, L, n, blk, d;
   int Sq, Sk;           // rows of the query / key tensors
-  int nw;               // wavefronts per workgroup (4 or 8)
+  int nw;               // wavefronts per workgroup
+  int qpw;              // query slots per wavefront (32 or 64)
   int rows_per_wg;      // query rows per workgroup (per half in HYBRID)
   int n_qtiles;         // query tiles per (batch, kv head)
   int n_splits;         // key splits (DECODE/CAUSAL only; 1 = no combine)
