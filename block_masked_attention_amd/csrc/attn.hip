@@ -76,8 +76,11 @@ __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
 // One workgroup = NW wavefronts; a wavefront owns QPW query slots, handled as
 // QPW/32 MFMA column blocks that share every K and V operand read from LDS
 // (64 slots per wavefront halve the LDS traffic per FLOP of 32).
-template <int D, int NW, int QPW>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
+// STAGES = 3: the pipelined walk below (one workgroup per CU at d = 128).
+// STAGES = 2: a plain double-buffered walk whose smaller LDS footprint lets two
+// workgroups share a CU, for short query blocks over long caches.
+template <int D, int NW, int QPW, int STAGES>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) {
   constexpr int NQB = QPW / 32;               // 32-query column blocks per wavefront
   constexpr int NT = NW * 64;
   constexpr int KSTEPS = D / 16;              // MFMA k-steps of Q K^T
@@ -87,7 +90,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
   constexpr int CU = (TCH + NT - 1) / NT;     // chunks per thread per tile
   constexpr int TE = kBN * D;                 // elements of one K (or V) tile
   constexpr int STAGE = 2 * TE;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[3 * STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[STAGES * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -320,7 +323,40 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
   // The last iteration computes (and drops) scores of a duplicate tile, so
   // the loop body has no branch besides the rare rescale.
   const int nf = (F.hi - F.lo) / kBN;
-  if (nf > 0) {
+  if (STAGES == 2 && nf > 0) {
+    // double-buffered: tile i+1 is stored and tile i+2 fetched after tile i
+    gload(F.lo, F.lo + kBN);
+    lstore(smem);
+    {
+      const int t = F.lo + imin(1, nf - 1) * kBN;
+      gload(t, t + kBN);
+    }
+    __syncthreads();
+    int st = 0;
+#pragma unroll 1
+    for (int i = 0; i < nf; ++i) {
+      const uint16_t* cur = smem + st * STAGE;
+      f32x16 sa[NQB], sb[NQB];
+      bf16x8 pb[NQB][2];
+      float alpha[NQB];
+      qk_sub(cur, 0, sa);
+      qk_sub(cur, 1, sb);
+      softmax_sub(sa, pb, alpha);
+      rescale(alpha);
+      pv_sub(cur, 0, pb);
+      softmax_sub(sb, pb, alpha);
+      rescale(alpha);
+      pv_sub(cur, 1, pb);
+      lstore(smem + (st ^ 1) * STAGE);
+      {
+        const int t = F.lo + imin(i + 2, nf - 1) * kBN;
+        gload(t, t + kBN);
+      }
+      __syncthreads();
+      st ^= 1;
+    }
+  }
+  if (STAGES == 3 && nf > 0) {
     gload(F.lo, F.lo + kBN);
     lstore(smem);
     {
@@ -336,8 +372,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
     int st = 0;
 #pragma unroll 1
     for (int i = 0; i < nf; ++i) {
-      const int stn = st == 2 ? 0 : st + 1;
-      const int stp = stn == 2 ? 0 : stn + 1;
+      const int stn = st == STAGES - 1 ? 0 : st + 1;
+      const int stp = stn == STAGES - 1 ? 0 : stn + 1;
       const uint16_t* cur = smem + st * STAGE;
       bf16x8 pb[NQB][2];
       float alpha[NQB];
@@ -517,7 +553,7 @@ int attn_make_plan(int B, int Hq, int Hkv, int L, int d, int block, int mode, At
     // Split the keys when (batch x kv head x query tile) alone cannot keep
     // every CU streaming; each split keeps at least 4 key tiles.
     const long long items = (long long)B * Hkv * x.n_qtiles;
-    const long long target = 2048;
+    const long long target = 512;      // two resident workgroups per CU
     int splits = (int)((target + items - 1) / items);
     const int max_splits = (L + 4 * kBN - 1) / (4 * kBN);
     if (splits > max_splits) splits = max_splits;
@@ -542,15 +578,15 @@ int attn_make_plan(int B, int Hq, int Hkv, int L, int d, int block, int mode, At
   return 0;
 }
 
-template <int D, int NW, int QPW>
+template <int D, int NW, int QPW, int STAGES>
 static hipError_t launch_main(const AttnArgs& a, long long grid, hipStream_t st) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, QPW>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, QPW, STAGES>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a);
   return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_d(const AttnPlan& p, const AttnArgs& a, hipStream_t st) {
-  hipError_t e = p.nw == 8 ? launch_main<D, 8, 32>(a, p.grid, st) : launch_main<D, 4, 32>(a, p.grid, st);
+  hipError_t e = p.nw == 8 ? launch_main<D, 8, 32, 3>(a, p.grid, st) : launch_main<D, 4, 32, 2>(a, p.grid, st);
   if (e != hipSuccess || p.n_splits == 1) return e;
   const long long rows = (long long)p.B * p.Hq * p.n;
   const long long threads = rows * (D / 4);
