@@ -88,6 +88,7 @@ __global__ __launch_bounds__(kCommitThreads) void stream_kernel(const void* __re
                                                                 const uint8_t* __restrict__ masked,
                                                                 Partial* __restrict__ part, int V,
                                                                 int n_chunks, int vec_ok) {
+  constexpr int VPT = kChunk / (8 * kCommitThreads);   // 8-value vectors per thread
   const int bid = blockIdx.x;
   const int t = bid / n_chunks;
   const int c = bid - t * n_chunks;
@@ -99,7 +100,61 @@ __global__ __launch_bounds__(kCommitThreads) void stream_kernel(const void* __re
   const int c1 = min(V, c0 + kChunk);
 
   Stat s{-INFINITY, 0.f, INT_MAX};
-  if (vec_ok) {
+  if (vec_ok && c1 - c0 == kChunk) {
+    // Whole chunk: every load of the thread is issued before any arithmetic
+    // (vector v covers values c0 + 8*(v*256 + tid) + 0..7, so a wavefront
+    // reads 1 KB contiguous per load and a thread's indices increase with v).
+    float x[VPT][8];
+    if (BF16) {
+      u32x4 w[VPT];
+#pragma unroll
+      for (int v = 0; v < VPT; ++v)
+        w[v] = __builtin_nontemporal_load((const u32x4*)(row + (size_t)(c0 + 8 * (v * kCommitThreads + tid)) * 2));
+#pragma unroll
+      for (int v = 0; v < VPT; ++v)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[v][2 * e] = bf16_lo(w[v][e]);
+          x[v][2 * e + 1] = bf16_hi(w[v][e]);
+        }
+    } else {
+      f32x4 w[VPT][2];
+#pragma unroll
+      for (int v = 0; v < VPT; ++v)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          w[v][h] = __builtin_nontemporal_load(
+              (const f32x4*)(row + (size_t)(c0 + 8 * (v * kCommitThreads + tid)) * 4 + 16 * h));
+#pragma unroll
+      for (int v = 0; v < VPT; ++v)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[v][e] = w[v][e >> 2][e & 3];
+    }
+    // pass 1: largest value and its lowest index
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+      float lm = x[v][0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) lm = fmaxf(lm, x[v][e]);
+      if (lm > s.m) {
+        int idx = 7;
+#pragma unroll
+        for (int e = 6; e >= 0; --e) idx = x[v][e] == lm ? e : idx;
+        s.m = lm;
+        s.a = c0 + 8 * (v * kCommitThreads + tid) + idx;
+      }
+    }
+    // pass 2: Z against that maximum
+    if (WITH_Z) {
+      const float nb = -s.m * kLog2e;
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < VPT; ++v)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e & 3] += exp2_fast(fmaf(x[v][e], kLog2e, nb));
+      s.z = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    }
+  } else if (vec_ok) {
     // 8 consecutive values per step: one 16-byte load (bf16) or two (fp32).
     for (int base = c0 + 8 * tid; base < c1; base += 8 * kCommitThreads) {
       float x[8];
