@@ -123,7 +123,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
   // ---- my query slots (one per column block)
   int qrow[NQB], head[NQB];
   bool valid[NQB];
-  Span A[NQB], C[NQB];
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     if (a.mode == kHybrid) {
@@ -143,9 +142,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       qrow[qb] = r;
       head[qb] = g * a.G + (s - rloc * a.G);
     }
-    A[qb] = Span{0, 0};
-    C[qb] = Span{0, 0};
-    if (valid[qb]) row_spans(a.mode, a.L, a.n, a.blk, qrow[qb], A[qb], C[qb]);
   }
 
   // ---- key ranges: F is walked by the pipelined loop (every row of the
@@ -305,6 +301,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       m_run[qb] = m_use;
     }
   };
+  // Keep the softmax of a subtile ahead of the (rarely taken) rescale branch,
+  // so its exponentials overlap the score MFMAs issued before it instead of
+  // being sunk into the block of the P V MFMAs that consume them.
+  auto pin = [&](bf16x8 (&pb)[NQB][2], float (&alpha)[NQB]) {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      asm volatile("" : "+v"(pb[qb][0]), "+v"(pb[qb][1]), "+v"(alpha[qb]));
+    }
+  };
   auto rescale = [&](const float (&alpha)[NQB]) {
     bool any = false;
 #pragma unroll
@@ -322,15 +327,81 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
   // of the current one; tile t+2 is stored and tile t+3 fetched during P V.
   // The last iteration computes (and drops) scores of a duplicate tile, so
   // the loop body has no branch besides the rare rescale.
+  // ---- the walk: the nf tiles of F, then the tiles of R1 and of R2.  One
+  // prefetch pipeline covers all of them; F tiles take the branch-free fast
+  // body, the others are classified per wavefront.  Prefetches past the end
+  // repeat the last tile (harmless, never computed).
   const int nf = (F.hi - F.lo) / kBN;
-  if (STAGES == 2 && nf > 0) {
-    // double-buffered: tile i+1 is stored and tile i+2 fetched after tile i
-    gload(F.lo, F.lo + kBN);
-    lstore(smem);
-    {
-      const int t = F.lo + imin(1, nf - 1) * kBN;
-      gload(t, t + kBN);
+  const int n1 = R1.hi > R1.lo ? (R1.hi - R1.lo + kBN - 1) / kBN : 0;
+  const int n2 = R2.hi > R2.lo ? (R2.hi - R2.lo + kBN - 1) / kBN : 0;
+  const int nt = nf + n1 + n2;
+  auto tile = [&](int j, int& t0, int& t1) {
+    j = imin(j, nt - 1);
+    if (j < nf) {
+      t0 = F.lo + j * kBN;
+      t1 = t0 + kBN;
+    } else if (j < nf + n1) {
+      t0 = R1.lo + (j - nf) * kBN;
+      t1 = imin(R1.hi, t0 + kBN);
+    } else {
+      t0 = R2.lo + (j - nf - n1) * kBN;
+      t1 = imin(R2.hi, t0 + kBN);
     }
+  };
+  auto fetch = [&](int j) {
+    int t0, t1;
+    tile(j, t0, t1);
+    gload(t0, t1);
+  };
+  // boundary tile j held in stage st: per-wavefront FULL / EMPTY / PARTIAL
+  auto slow_tile = [&](const uint16_t* st, int j) {
+    int t0, t1;
+    tile(j, t0, t1);
+    Span A[NQB], C[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      A[qb] = Span{0, 0};
+      C[qb] = Span{0, 0};
+      if (valid[qb]) row_spans(a.mode, a.L, a.n, a.blk, qrow[qb], A[qb], C[qb]);
+    }
+#pragma unroll 1
+    for (int sub = 0; sub < 2; ++sub) {
+      const int e0 = t0 + 32 * sub, e1 = imin(t1, e0 + 32);
+      if (e0 >= e1) break;
+      bool full = true, empty = true;
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const int c = inside(A[qb], e0, e1) + inside(C[qb], e0, e1);
+        full &= !valid[qb] || (e1 - e0 == 32 && c == 32);
+        empty &= !valid[qb] || c == 0;
+      }
+      if (__all(empty)) continue;
+      f32x16 s[NQB];
+      qk_sub(st, sub, s);
+      if (!__all(full)) {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int jj = e0 + 8 * (i >> 2) + 4 * hb + (i & 3);
+            const bool ok = jj < e1 && (in_span(A[qb], jj) || in_span(C[qb], jj));
+            s[qb][i] = ok ? s[qb][i] : -INFINITY;
+          }
+        }
+      }
+      bf16x8 pb[NQB][2];
+      float alpha[NQB];
+      softmax_sub(s, pb, alpha);
+      rescale(alpha);
+      pv_sub(st, sub, pb);
+    }
+  };
+
+  if (STAGES == 2 && nt > 0) {
+    // double-buffered: tile i+1 is stored and tile i+2 fetched after tile i
+    fetch(0);
+    lstore(smem);
+    fetch(1);
     __syncthreads();
     int st = 0;
 #pragma unroll 1
@@ -348,27 +419,34 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       rescale(alpha);
       pv_sub(cur, 1, pb);
       lstore(smem + (st ^ 1) * STAGE);
-      {
-        const int t = F.lo + imin(i + 2, nf - 1) * kBN;
-        gload(t, t + kBN);
-      }
+      fetch(i + 2);
+      __syncthreads();
+      st ^= 1;
+    }
+#pragma unroll 1
+    for (int i = nf; i < nt; ++i) {
+      slow_tile(smem + st * STAGE, i);
+      lstore(smem + (st ^ 1) * STAGE);
+      fetch(i + 2);
       __syncthreads();
       st ^= 1;
     }
   }
-  if (STAGES == 3 && nf > 0) {
-    gload(F.lo, F.lo + kBN);
+
+  // ---- pipelined walk (stage t%3 holds tile t).  Per fast tile: the MFMAs
+  // of the next subtile's scores are issued together with the softmax of the
+  // current one; tile t+2 is stored and tile t+3 fetched during P V.  The
+  // scores of subtile 0 of the tile after the last fast one are computed and
+  // dropped, so the fast body has no branch besides the rare rescale.
+  if (STAGES == 3 && nt > 0) {
+    fetch(0);
     lstore(smem);
-    {
-      const int t = F.lo + imin(1, nf - 1) * kBN;
-      gload(t, t + kBN);
-      lstore(smem + STAGE);
-      const int t2 = F.lo + imin(2, nf - 1) * kBN;
-      gload(t2, t2 + kBN);
-    }
+    fetch(1);
+    lstore(smem + STAGE);
+    fetch(2);
     __syncthreads();
     f32x16 sa[NQB], sb[NQB];
-    qk_sub(smem, 0, sa);
+    if (nf > 0) qk_sub(smem, 0, sa);
     int st = 0;
 #pragma unroll 1
     for (int i = 0; i < nf; ++i) {
@@ -379,64 +457,28 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       float alpha[NQB];
       qk_sub(cur, 1, sb);
       softmax_sub(sa, pb, alpha);
+      pin(pb, alpha);
       rescale(alpha);
       pv_sub(cur, 0, pb);
       lstore(smem + stp * STAGE);
       qk_sub(smem + stn * STAGE, 0, sa);
       softmax_sub(sb, pb, alpha);
+      pin(pb, alpha);
       rescale(alpha);
       pv_sub(cur, 1, pb);
-      {
-        const int t = F.lo + imin(i + 3, nf - 1) * kBN;
-        gload(t, t + kBN);
-      }
+      fetch(i + 3);
       __syncthreads();
       st = stn;
     }
-  }
-
-  // ---- boundary tiles: per-wavefront FULL / EMPTY / PARTIAL classification
 #pragma unroll 1
-  for (int seg = 0; seg < 2; ++seg) {
-    const Span R = seg == 0 ? R1 : R2;
-#pragma unroll 1
-    for (int t0 = R.lo; t0 < R.hi; t0 += kBN) {
-      const int t1 = imin(R.hi, t0 + kBN);
-      gload(t0, t1);
-      lstore(smem);
+    for (int i = nf; i < nt; ++i) {
+      const int stn = st == STAGES - 1 ? 0 : st + 1;
+      const int stp = stn == STAGES - 1 ? 0 : stn + 1;
+      slow_tile(smem + st * STAGE, i);
+      lstore(smem + stp * STAGE);
+      fetch(i + 3);
       __syncthreads();
-#pragma unroll 1
-      for (int sub = 0; sub < 2; ++sub) {
-        const int e0 = t0 + 32 * sub, e1 = imin(t1, e0 + 32);
-        if (e0 >= e1) break;
-        bool full = true, empty = true;
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-          const int c = inside(A[qb], e0, e1) + inside(C[qb], e0, e1);
-          full &= !valid[qb] || (e1 - e0 == 32 && c == 32);
-          empty &= !valid[qb] || c == 0;
-        }
-        if (__all(empty)) continue;
-        f32x16 s[NQB];
-        qk_sub(smem, sub, s);
-        if (!__all(full)) {
-#pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int j = e0 + 8 * (i >> 2) + 4 * hb + (i & 3);
-              const bool ok = j < e1 && (in_span(A[qb], j) || in_span(C[qb], j));
-              s[qb][i] = ok ? s[qb][i] : -INFINITY;
-            }
-          }
-        }
-        bf16x8 pb[NQB][2];
-        float alpha[NQB];
-        softmax_sub(s, pb, alpha);
-        rescale(alpha);
-        pv_sub(smem, sub, pb);
-      }
-      __syncthreads();
+      st = stn;
     }
   }
 
