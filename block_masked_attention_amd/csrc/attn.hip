@@ -67,6 +67,17 @@ __device__ __forceinline__ int chunk_off(int r, int c) {  // element offset of c
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
+// 16 bytes per lane from global memory straight into LDS: lane i of the
+// wavefront writes lds_run + 16*i (lds_run must be the same for every lane).
+// Written as inline assembly so that the compiler does not pair every later
+// LDS read with a wait for all such loads: the kernel waits for them itself
+// (s_waitcnt vmcnt) before the barrier that publishes a stage.  M0 is set in
+// the same statement and used by nothing else in these kernels.
+__device__ __forceinline__ void lds_dma16(const uint16_t* g, const uint16_t* lds_run) {
+  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_run);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(base) : "memory");
+}
+
 // ds_read_b64_tr_b16: within each 16-lane group, lane j receives element
 // (j & 3) of the 4-element row read by lane 4*e + (j >> 2), for e = 0..3.
 __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
@@ -76,9 +87,11 @@ __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
 // One workgroup = NW wavefronts; a wavefront owns QPW query slots, handled as
 // QPW/32 MFMA column blocks that share every K and V operand read from LDS
 // (64 slots per wavefront halve the LDS traffic per FLOP of 32).
-// STAGES = 3: the pipelined walk below (one workgroup per CU at d = 128).
-// STAGES = 2: a plain double-buffered walk whose smaller LDS footprint lets two
-// workgroups share a CU, for short query blocks over long caches.
+// STAGES = 4: the DMA-fed pipelined walk (one 8-wave workgroup per CU at
+// d = 128) for long query ranges (training form, prefill).
+// STAGES = 2: a register-staged double-buffered walk whose smaller LDS
+// footprint lets two 4-wave workgroups share a CU, for short query blocks
+// over long caches (decode, verify).
 template <int D, int NW, int QPW, int STAGES>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) {
   constexpr int NQB = QPW / 32;               // 32-query column blocks per wavefront
@@ -353,6 +366,47 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
     tile(j, t0, t1);
     gload(t0, t1);
   };
+  // Tile j straight from global memory into an LDS stage (no registers):
+  // each lane of a wavefront's load lands 16 bytes at its lane slot of a
+  // contiguous 1 KB run, so the lane picks the global chunk that the
+  // permuted layout puts there.
+  constexpr int DJ = TCH >= NT ? TCH / NT : 1;   // DMA loads per wavefront per matrix
+  auto dma = [&](int j, uint16_t* st) {
+    int t0, t1;
+    tile(j, t0, t1);
+#pragma unroll
+    for (int q = 0; q < DJ; ++q) {
+      const int run = w * DJ + q;                 // 64-chunk run of the tile
+      if (run * 64 < TCH) {
+        const int pos = run * 64 + lane;
+        const int r = pos / CPR, pc = pos % CPR;
+        const int c = pc ^ (swz<D>(r) & (CPR - 1));
+        const size_t off = (size_t)imin(t0 + r, t1 - 1) * D + 8 * c;
+        const uint16_t* dst = st + run * 64 * 8;
+        lds_dma16(kbase + off, dst);
+        lds_dma16(vbase + off, dst + TE);
+      }
+    }
+  };
+  // All but the newest tile's DMA loads (and every LDS access) have landed;
+  // then the workgroup barrier (without the fence of __syncthreads, which
+  // would also wait for the newest loads).
+  // Every outstanding load (DMA included) has landed, then the barrier.
+  // __syncthreads() would not wait for the DMA loads: the compiler does not
+  // know about them.
+  auto drain = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  auto settle = [&]() {
+    constexpr int N = 2 * DJ;
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
   // boundary tile j held in stage st: per-wavefront FULL / EMPTY / PARTIAL
   auto slow_tile = [&](const uint16_t* st, int j) {
     int t0, t1;
@@ -433,26 +487,22 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
     }
   }
 
-  // ---- pipelined walk (stage t%3 holds tile t).  Per fast tile: the MFMAs
-  // of the next subtile's scores are issued together with the softmax of the
-  // current one; tile t+2 is stored and tile t+3 fetched during P V.  The
-  // scores of subtile 0 of the tile after the last fast one are computed and
-  // dropped, so the fast body has no branch besides the rare rescale.
-  if (STAGES == 3 && nt > 0) {
-    fetch(0);
-    lstore(smem);
-    fetch(1);
-    lstore(smem + STAGE);
-    fetch(2);
-    __syncthreads();
+  // ---- DMA-fed walk (stage t%4 holds tile t, filled three tiles ahead).
+  // Per fast tile: the MFMAs of the next subtile's scores are issued with
+  // the softmax of the current one; the scores of subtile 0 of the tile
+  // after the last fast one are computed and dropped, so the fast body has
+  // no branch besides the rare rescale.
+  if (STAGES == 4 && nt > 0) {
+    dma(0, smem);
+    dma(1, smem + STAGE);
+    dma(2, smem + 2 * STAGE);
+    drain();
     f32x16 sa[NQB], sb[NQB];
     if (nf > 0) qk_sub(smem, 0, sa);
-    int st = 0;
 #pragma unroll 1
     for (int i = 0; i < nf; ++i) {
-      const int stn = st == STAGES - 1 ? 0 : st + 1;
-      const int stp = stn == STAGES - 1 ? 0 : stn + 1;
-      const uint16_t* cur = smem + st * STAGE;
+      const uint16_t* cur = smem + (i & 3) * STAGE;
+      dma(i + 3, smem + ((i + 3) & 3) * STAGE);
       bf16x8 pb[NQB][2];
       float alpha[NQB];
       qk_sub(cur, 1, sb);
@@ -460,26 +510,20 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       pin(pb, alpha);
       rescale(alpha);
       pv_sub(cur, 0, pb);
-      lstore(smem + stp * STAGE);
-      qk_sub(smem + stn * STAGE, 0, sa);
+      qk_sub(smem + ((i + 1) & 3) * STAGE, 0, sa);
       softmax_sub(sb, pb, alpha);
       pin(pb, alpha);
       rescale(alpha);
       pv_sub(cur, 1, pb);
-      fetch(i + 3);
-      __syncthreads();
-      st = stn;
+      settle();
     }
 #pragma unroll 1
     for (int i = nf; i < nt; ++i) {
-      const int stn = st == STAGES - 1 ? 0 : st + 1;
-      const int stp = stn == STAGES - 1 ? 0 : stn + 1;
-      slow_tile(smem + st * STAGE, i);
-      lstore(smem + stp * STAGE);
-      fetch(i + 3);
-      __syncthreads();
-      st = stn;
+      dma(i + 3, smem + ((i + 3) & 3) * STAGE);
+      slow_tile(smem + (i & 3) * STAGE, i);
+      settle();
     }
+    drain();   // the last prefetches (repeats of the last tile) land before exit
   }
 
   // ---- epilogue: lane (ql, hb) holds d = 32*dt + 8*(i/4) + 4*hb + (i%4)
@@ -628,7 +672,7 @@ static hipError_t launch_main(const AttnArgs& a, long long grid, hipStream_t st)
 
 template <int D>
 static hipError_t launch_d(const AttnPlan& p, const AttnArgs& a, hipStream_t st) {
-  hipError_t e = p.nw == 8 ? launch_main<D, 8, 32, 3>(a, p.grid, st) : launch_main<D, 4, 32, 2>(a, p.grid, st);
+  hipError_t e = p.nw == 8 ? launch_main<D, 8, 32, 4>(a, p.grid, st) : launch_main<D, 4, 32, 2>(a, p.grid, st);
   if (e != hipSuccess || p.n_splits == 1) return e;
   const long long rows = (long long)p.B * p.Hq * p.n;
   const long long threads = rows * (D / 4);
