@@ -264,7 +264,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       for (int dt = 0; dt < DT; ++dt) {
         const s16x4 lo = lds_read_tr(vt + v_lo[dt]);
         const s16x4 hi = lds_read_tr(vt + v_hi[dt]);
-        typedef short s16x8 __attribute__((ext_vector_type(8)));
         const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
@@ -314,14 +313,66 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       m_run[qb] = m_use;
     }
   };
-  // Keep the softmax of a subtile ahead of the (rarely taken) rescale branch,
-  // so its exponentials overlap the score MFMAs issued before it instead of
-  // being sunk into the block of the P V MFMAs that consume them.
-  auto pin = [&](bf16x8 (&pb)[NQB][2], float (&alpha)[NQB]) {
+  // Softmax of a subtile whose keys every row sees (the pipelined walk),
+  // against the running max as it stands.  The weights are summed from their
+  // bf16 values (the values P V uses).  If some lane's sum reaches 2^8 (a
+  // weight may then exceed 2^8, or the max is still unset) the running max
+  // moves to the subtile's max, O and l are scaled by alpha <= 1 and the
+  // subtile is redone with every weight <= 1.  Usually no max is taken.
+  auto softmax_fast = [&](const f32x16 (&s)[NQB], bf16x8 (&pb)[NQB][2]) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+    float ls[NQB];
+    auto expo = [&](int qb, float nb) {
+      float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = exp2_fast(fmaf(s[qb][8 * kk + 2 * e], sl2, nb));
+          const float p1 = exp2_fast(fmaf(s[qb][8 * kk + 2 * e + 1], sl2, nb));
+          // Summed from this temporary: reading the pair back out of pk[e]
+          // for the dot product is miscompiled by this toolchain.
+          const unsigned pw = pack_bf16x2(p0, p1);
+          pk[e] = pw;
+          if (e & 1) l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw), one2, l1, false);
+          else l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw), one2, l0, false);
+        }
+        pb[qb][kk] = __builtin_bit_cast(bf16x8, pk);
+      }
+      ls[qb] = l0 + l1;
+    };
+    bool bad = false;
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
-      asm volatile("" : "+v"(pb[qb][0]), "+v"(pb[qb][1]), "+v"(alpha[qb]));
+      expo(qb, -m_run[qb] * sl2);
+      bad |= !(ls[qb] < 256.f);
     }
+    if (__builtin_expect(__any(bad), 0)) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        float mt = s[qb][0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[qb][i]);
+        const float m_use = fmaxf(m_run[qb], half_max(mt));
+        const float alpha = exp2_fast((m_run[qb] - m_use) * sl2);   // 0 while the max is unset
+        expo(qb, -m_use * sl2);
+        m_run[qb] = m_use;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[qb][dt] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) l_run[qb] += ls[qb];
+  };
+  // Keep the softmax of a subtile where it is written, so its exponentials
+  // overlap the score MFMAs issued before it instead of being sunk into the
+  // block of the P V MFMAs that consume them.
+  auto pin = [&](bf16x8 (&pb)[NQB][2]) {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) asm volatile("" : "+v"(pb[qb][0]), "+v"(pb[qb][1]));
   };
   auto rescale = [&](const float (&alpha)[NQB]) {
     bool any = false;
@@ -463,14 +514,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       const uint16_t* cur = smem + st * STAGE;
       f32x16 sa[NQB], sb[NQB];
       bf16x8 pb[NQB][2];
-      float alpha[NQB];
       qk_sub(cur, 0, sa);
       qk_sub(cur, 1, sb);
-      softmax_sub(sa, pb, alpha);
-      rescale(alpha);
+      softmax_fast(sa, pb);
       pv_sub(cur, 0, pb);
-      softmax_sub(sb, pb, alpha);
-      rescale(alpha);
+      softmax_fast(sb, pb);
       pv_sub(cur, 1, pb);
       lstore(smem + (st ^ 1) * STAGE);
       fetch(i + 2);
@@ -504,16 +552,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       const uint16_t* cur = smem + (i & 3) * STAGE;
       dma(i + 3, smem + ((i + 3) & 3) * STAGE);
       bf16x8 pb[NQB][2];
-      float alpha[NQB];
       qk_sub(cur, 1, sb);
-      softmax_sub(sa, pb, alpha);
-      pin(pb, alpha);
-      rescale(alpha);
+      softmax_fast(sa, pb);
+      pin(pb);
       pv_sub(cur, 0, pb);
       qk_sub(smem + ((i + 1) & 3) * STAGE, 0, sa);
-      softmax_sub(sb, pb, alpha);
-      pin(pb, alpha);
-      rescale(alpha);
+      softmax_fast(sb, pb);
+      pin(pb);
       pv_sub(cur, 1, pb);
       settle();
     }
