@@ -36,7 +36,16 @@ struct AttnArgs {
   float* part_ml;   // [split][B*Hq*n][2] (running max in log2 units, row sum)
   int B, Hq, Hkv, G, mode, L, n, blk, Sq, Sk;
   int rows_per_wg, n_qtiles, n_splits, split_keys, pairs_per_xcd;
+  int n_items;      // work items (batch x kv head x query tile x key split)
   float sl2;        // log2(e) / sqrt(D)
+};
+
+// Geometry of one work item: its (batch, kv head) pair, query tile and key
+// split, and the key ranges its rows need (see the kernel).
+struct Geom {
+  Span F, R1, R2;
+  int nf, n1, nt;
+  int pair, qt, split;
 };
 
 __device__ __forceinline__ bool in_span(const Span& s, int j) {
@@ -111,90 +120,113 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
   const int ql = lane & 31;
   const int hb = lane >> 5;
 
-  // ---- which (batch, kv head, query tile, key split) this workgroup serves
+  // ---- work items.  The canonical order (index -> batch, kv head, query
+  // tile, key split) hands out the heaviest query tiles first.  With
+  // pairs_per_xcd > 0, index i runs on XCD i % 8 (workgroups are dealt to the
+  // 8 XCDs round-robin) and every query tile of a (batch, kv head) maps to
+  // one XCD, so its K/V stays in that XCD's L2.
   const int P = a.B * a.Hkv;
-  int pair, qt, split = 0;
-  {
-    const int bid = blockIdx.x;
+  // key ranges of an item: F is walked by the pipelined loop (every row of
+  // the item may see every key of it); R1 and R2 are the remaining keys the
+  // rows need, walked tile by tile with per-wavefront classification.
+  auto geom = [&](int idx, Geom& gm) {
     if (a.pairs_per_xcd > 0) {
-      // Workgroups are dealt to the 8 XCDs round-robin: keep every query tile
-      // of a (batch, kv head) on one XCD so its K/V stays in that L2, and
-      // hand out the heaviest (latest) query tiles first.
-      const int xcd = bid & 7, i = bid >> 3;
-      pair = xcd * a.pairs_per_xcd + i % a.pairs_per_xcd;
-      qt = a.n_qtiles - 1 - i / a.pairs_per_xcd;
+      const int xcd = idx & 7, i = idx >> 3;
+      gm.pair = xcd * a.pairs_per_xcd + i % a.pairs_per_xcd;
+      gm.qt = a.n_qtiles - 1 - i / a.pairs_per_xcd;
+      gm.split = 0;
     } else {
-      split = bid % a.n_splits;
-      const int rest = bid / a.n_splits;
-      pair = rest % P;
-      qt = a.n_qtiles - 1 - rest / P;
+      gm.split = idx % a.n_splits;
+      const int rest = idx / a.n_splits;
+      gm.pair = rest % P;
+      gm.qt = a.n_qtiles - 1 - rest / P;
     }
-  }
-  const int b = pair / a.Hkv;
-  const int g = pair - b * a.Hkv;
+    Span F{0, 0}, R1{0, 0}, R2{0, 0};
+    if (a.mode == kHybrid) {
+      const int p0 = gm.qt * a.rows_per_wg;
+      const int p1 = imin(a.L, p0 + a.rows_per_wg);
+      const int e = imin(a.L, ((p1 - 1) / a.blk + 1) * a.blk);
+      const int s_min = (p0 / a.blk) * a.blk;   // clean prefix every row of the item sees
+      F = Span{a.L, a.L + (s_min / kBN) * kBN};
+      R1 = Span{F.hi, a.L + e};                 // rest of the clean prefix / own clean blocks
+      R2 = Span{s_min, e};                      // noisy blocks of these rows
+    } else {
+      const int r0 = gm.qt * a.rows_per_wg;
+      const int r1 = imin(a.n, r0 + a.rows_per_wg);
+      const int lo = gm.split * a.split_keys;
+      const int hi = imin(a.mode == kDecode ? a.L : a.L - a.n + r1, lo + a.split_keys);
+      const int full_hi = imin(hi, a.mode == kDecode ? a.L : a.L - a.n + r0 + 1);
+      const int nfull = full_hi > lo ? (full_hi - lo) / kBN : 0;
+      F = Span{lo, lo + nfull * kBN};
+      R1 = Span{F.hi, imax(F.hi, hi)};
+    }
+    gm.F = F;
+    gm.R1 = R1;
+    gm.R2 = R2;
+    gm.nf = (F.hi - F.lo) / kBN;
+    gm.n1 = R1.hi > R1.lo ? (R1.hi - R1.lo + kBN - 1) / kBN : 0;
+    const int n2 = R2.hi > R2.lo ? (R2.hi - R2.lo + kBN - 1) / kBN : 0;
+    gm.nt = gm.nf + gm.n1 + n2;
+  };
+  // first and last key of tile j of an item (j clamped to the last tile)
+  auto tile_in = [&](const Geom& gm, int j, int& t0, int& t1) {
+    j = imin(j, gm.nt - 1);
+    if (j < gm.nf) {
+      t0 = gm.F.lo + j * kBN;
+      t1 = t0 + kBN;
+    } else if (j < gm.nf + gm.n1) {
+      t0 = gm.R1.lo + (j - gm.nf) * kBN;
+      t1 = imin(gm.R1.hi, t0 + kBN);
+    } else {
+      t0 = gm.R2.lo + (j - gm.nf - gm.n1) * kBN;
+      t1 = imin(gm.R2.hi, t0 + kBN);
+    }
+  };
 
-  // ---- my query slots (one per column block)
+  // ---- the item being computed
+  Geom cur{};
+  int b = 0, g = 0;
+  const uint16_t* kbase = a.k;
+  const uint16_t* vbase = a.v;
   int qrow[NQB], head[NQB];
   bool valid[NQB];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    if (a.mode == kHybrid) {
-      const int per_half = NW / 2;
-      const int half = w / per_half;
-      const int s = ((w - half * per_half) * NQB + qb) * 32 + ql;
-      const int rloc = s / a.G;
-      const int pos = qt * a.rows_per_wg + rloc;
-      valid[qb] = rloc < a.rows_per_wg && pos < a.L;
-      qrow[qb] = half * a.L + pos;
-      head[qb] = g * a.G + (s - rloc * a.G);
-    } else {
-      const int s = (w * NQB + qb) * 32 + ql;
-      const int rloc = s / a.G;
-      const int r = qt * a.rows_per_wg + rloc;
-      valid[qb] = rloc < a.rows_per_wg && r < a.n;
-      qrow[qb] = r;
-      head[qb] = g * a.G + (s - rloc * a.G);
-    }
-  }
-
-  // ---- key ranges: F is walked by the pipelined loop (every row of the
-  // workgroup may see every key of it); R1 and R2 are the remaining keys the
-  // rows need, walked tile by tile with per-wavefront classification.
-  Span F{0, 0}, R1{0, 0}, R2{0, 0};
-  if (a.mode == kHybrid) {
-    const int p0 = qt * a.rows_per_wg;
-    const int p1 = imin(a.L, p0 + a.rows_per_wg);
-    const int e = imin(a.L, ((p1 - 1) / a.blk + 1) * a.blk);
-    const int s_min = (p0 / a.blk) * a.blk;     // clean prefix every row of the workgroup sees
-    F = Span{a.L, a.L + (s_min / kBN) * kBN};
-    R1 = Span{F.hi, a.L + e};                   // rest of the clean prefix / own clean blocks
-    R2 = Span{s_min, e};                        // noisy blocks of these rows
-  } else {
-    const int r0 = qt * a.rows_per_wg;
-    const int r1 = imin(a.n, r0 + a.rows_per_wg);
-    const int lo = split * a.split_keys;
-    const int hi = imin(a.mode == kDecode ? a.L : a.L - a.n + r1, lo + a.split_keys);
-    const int full_hi = imin(hi, a.mode == kDecode ? a.L : a.L - a.n + r0 + 1);
-    const int nfull = full_hi > lo ? (full_hi - lo) / kBN : 0;
-    F = Span{lo, lo + nfull * kBN};
-    R1 = Span{F.hi, imax(F.hi, hi)};
-  }
-
-  // ---- Q operands in registers: lane (ql, hb) holds d = 16*ks + 8*hb + 0..7
   bf16x8 qreg[NQB][KSTEPS];
+  // Switch to item idx: its geometry, my query slots (one per column block)
+  // and their Q operands (lane (ql, hb) holds d = 16*ks + 8*hb + 0..7).
+  auto begin_item = [&](int idx) {
+    geom(idx, cur);
+    b = cur.pair / a.Hkv;
+    g = cur.pair - b * a.Hkv;
+    const size_t kvoff = (size_t)cur.pair * a.Sk * D;
+    kbase = a.k + kvoff;
+    vbase = a.v + kvoff;
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const uint16_t* qp = a.q + ((size_t)(b * a.Hq + head[qb]) * a.Sq + qrow[qb]) * D + 8 * hb;
+    for (int qb = 0; qb < NQB; ++qb) {
+      if (a.mode == kHybrid) {
+        const int per_half = NW / 2;
+        const int half = w / per_half;
+        const int s = ((w - half * per_half) * NQB + qb) * 32 + ql;
+        const int rloc = s / a.G;
+        const int pos = cur.qt * a.rows_per_wg + rloc;
+        valid[qb] = rloc < a.rows_per_wg && pos < a.L;
+        qrow[qb] = half * a.L + pos;
+        head[qb] = g * a.G + (s - rloc * a.G);
+      } else {
+        const int s = (w * NQB + qb) * 32 + ql;
+        const int rloc = s / a.G;
+        const int r = cur.qt * a.rows_per_wg + rloc;
+        valid[qb] = rloc < a.rows_per_wg && r < a.n;
+        qrow[qb] = r;
+        head[qb] = g * a.G + (s - rloc * a.G);
+      }
+      const uint16_t* qp = a.q + ((size_t)(b * a.Hq + head[qb]) * a.Sq + qrow[qb]) * D + 8 * hb;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      u32x4 x = valid[qb] ? *(const u32x4*)(qp + 16 * ks) : u32x4{0, 0, 0, 0};
-      qreg[qb][ks] = __builtin_bit_cast(bf16x8, x);
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        u32x4 x = valid[qb] ? *(const u32x4*)(qp + 16 * ks) : u32x4{0, 0, 0, 0};
+        qreg[qb][ks] = __builtin_bit_cast(bf16x8, x);
+      }
     }
-  }
-
-  const size_t kvoff = (size_t)(b * a.Hkv + g) * a.Sk * D;
-  const uint16_t* kbase = a.k + kvoff;
-  const uint16_t* vbase = a.v + kvoff;
+  };
 
   // lane-constant LDS offsets (elements, within a stage)
   const int k_row = ql * D;
@@ -251,10 +283,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
     }
   };
   f32x16 o[NQB][DT];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[qb][dt] = f32x16{};
   // O^T += V^T P^T for one 32-key subtile (two 16-key MFMA k-steps)
   auto pv_sub = [&](const uint16_t* st, int sub, const bf16x8 (&pb)[NQB][2]) {
 #pragma unroll
@@ -275,11 +303,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
   const float sl2 = a.sl2;
   const float thr = 8.f / sl2;   // keep the running max until scores exceed it by 2^8 in weight
   float m_run[NQB], l_run[NQB];
+  auto reset_acc = [&]() {
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
-  }
+    for (int qb = 0; qb < NQB; ++qb) {
+      m_run[qb] = -INFINITY;
+      l_run[qb] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[qb][dt] = f32x16{};
+    }
+  };
 
   // Online softmax of one 32-key subtile (lane = query of each column block,
   // 16 of the 32 keys).  The running max only moves when a score exceeds it
@@ -386,32 +418,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
     }
   };
 
-  // ---- pipelined walk over F (stage t%3 holds tile t).  Per tile: the
-  // MFMAs of the next subtile's scores are issued together with the softmax
-  // of the current one; tile t+2 is stored and tile t+3 fetched during P V.
-  // The last iteration computes (and drops) scores of a duplicate tile, so
-  // the loop body has no branch besides the rare rescale.
-  // ---- the walk: the nf tiles of F, then the tiles of R1 and of R2.  One
-  // prefetch pipeline covers all of them; F tiles take the branch-free fast
-  // body, the others are classified per wavefront.  Prefetches past the end
-  // repeat the last tile (harmless, never computed).
-  const int nf = (F.hi - F.lo) / kBN;
-  const int n1 = R1.hi > R1.lo ? (R1.hi - R1.lo + kBN - 1) / kBN : 0;
-  const int n2 = R2.hi > R2.lo ? (R2.hi - R2.lo + kBN - 1) / kBN : 0;
-  const int nt = nf + n1 + n2;
-  auto tile = [&](int j, int& t0, int& t1) {
-    j = imin(j, nt - 1);
-    if (j < nf) {
-      t0 = F.lo + j * kBN;
-      t1 = t0 + kBN;
-    } else if (j < nf + n1) {
-      t0 = R1.lo + (j - nf) * kBN;
-      t1 = imin(R1.hi, t0 + kBN);
-    } else {
-      t0 = R2.lo + (j - nf - n1) * kBN;
-      t1 = imin(R2.hi, t0 + kBN);
-    }
-  };
+  auto tile = [&](int j, int& t0, int& t1) { tile_in(cur, j, t0, t1); };
   auto fetch = [&](int j) {
     int t0, t1;
     tile(j, t0, t1);
@@ -422,9 +429,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
   // contiguous 1 KB run, so the lane picks the global chunk that the
   // permuted layout puts there.
   constexpr int DJ = TCH >= NT ? TCH / NT : 1;   // DMA loads per wavefront per matrix
-  auto dma = [&](int j, uint16_t* st) {
+  auto dma = [&](const Geom& gm, int j, uint16_t* st) {
     int t0, t1;
-    tile(j, t0, t1);
+    tile_in(gm, j, t0, t1);
+    const uint16_t* kb = a.k + (size_t)gm.pair * a.Sk * D;
+    const uint16_t* vb = a.v + (size_t)gm.pair * a.Sk * D;
 #pragma unroll
     for (int q = 0; q < DJ; ++q) {
       const int run = w * DJ + q;                 // 64-chunk run of the tile
@@ -434,8 +443,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
         const int c = pc ^ (swz<D>(r) & (CPR - 1));
         const size_t off = (size_t)imin(t0 + r, t1 - 1) * D + 8 * c;
         const uint16_t* dst = st + run * 64 * 8;
-        lds_dma16(kbase + off, dst);
-        lds_dma16(vbase + off, dst + TE);
+        lds_dma16(kb + off, dst);
+        lds_dma16(vb + off, dst + TE);
       }
     }
   };
@@ -502,111 +511,170 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
     }
   };
 
-  if (STAGES == 2 && nt > 0) {
-    // double-buffered: tile i+1 is stored and tile i+2 fetched after tile i
-    fetch(0);
-    lstore(smem);
-    fetch(1);
-    __syncthreads();
-    int st = 0;
-#pragma unroll 1
-    for (int i = 0; i < nf; ++i) {
-      const uint16_t* cur = smem + st * STAGE;
-      f32x16 sa[NQB], sb[NQB];
-      bf16x8 pb[NQB][2];
-      qk_sub(cur, 0, sa);
-      qk_sub(cur, 1, sb);
-      softmax_fast(sa, pb);
-      pv_sub(cur, 0, pb);
-      softmax_fast(sb, pb);
-      pv_sub(cur, 1, pb);
-      lstore(smem + (st ^ 1) * STAGE);
-      fetch(i + 2);
-      __syncthreads();
-      st ^= 1;
+  // ---- epilogue of the current item: lane (ql, hb) holds
+  // d = 32*dt + 8*(i/4) + 4*hb + (i%4)
+  auto finish = [&]() {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const float l_tot = half_sum(l_run[qb]);
+      if (!valid[qb]) continue;
+      if (a.n_splits == 1) {
+        const float inv = 1.f / l_tot;
+        uint16_t* op = a.out + ((size_t)(b * a.Hq + head[qb]) * a.Sq + qrow[qb]) * D + 4 * hb;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            u32x2 pk;
+            pk[0] = pack_bf16x2(o[qb][dt][4 * i4] * inv, o[qb][dt][4 * i4 + 1] * inv);
+            pk[1] = pack_bf16x2(o[qb][dt][4 * i4 + 2] * inv, o[qb][dt][4 * i4 + 3] * inv);
+            *(u32x2*)(op + 32 * dt + 8 * i4) = pk;
+          }
+        }
+      } else {
+        const size_t rows = (size_t)a.B * a.Hq * a.n;
+        const size_t row = (size_t)(b * a.Hq + head[qb]) * a.n + qrow[qb];
+        float* po = a.part_o + ((size_t)cur.split * rows + row) * D + 4 * hb;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            f32x4 x{o[qb][dt][4 * i4], o[qb][dt][4 * i4 + 1], o[qb][dt][4 * i4 + 2], o[qb][dt][4 * i4 + 3]};
+            *(f32x4*)(po + 32 * dt + 8 * i4) = x;
+          }
+        }
+        if (hb == 0) {
+          float* pm = a.part_ml + ((size_t)cur.split * rows + row) * 2;
+          pm[0] = m_run[qb] == -INFINITY ? -INFINITY : m_run[qb] * sl2;
+          pm[1] = l_tot;
+        }
+      }
     }
-#pragma unroll 1
-    for (int i = nf; i < nt; ++i) {
-      slow_tile(smem + st * STAGE, i);
-      lstore(smem + (st ^ 1) * STAGE);
-      fetch(i + 2);
-      __syncthreads();
-      st ^= 1;
-    }
-  }
+  };
 
-  // ---- DMA-fed walk (stage t%4 holds tile t, filled three tiles ahead).
-  // Per fast tile: the MFMAs of the next subtile's scores are issued with
-  // the softmax of the current one; the scores of subtile 0 of the tile
-  // after the last fast one are computed and dropped, so the fast body has
-  // no branch besides the rare rescale.
-  if (STAGES == 4 && nt > 0) {
-    dma(0, smem);
-    dma(1, smem + STAGE);
-    dma(2, smem + 2 * STAGE);
+  if constexpr (STAGES == 2) {
+    // One item per workgroup, double-buffered: tile i+1 is stored and tile
+    // i+2 fetched after tile i.
+    begin_item(blockIdx.x);
+    reset_acc();
+    const int nf = cur.nf, nt = cur.nt;
+    if (nt > 0) {
+      fetch(0);
+      lstore(smem);
+      fetch(1);
+      __syncthreads();
+      int st = 0;
+#pragma unroll 1
+      for (int i = 0; i < nf; ++i) {
+        const uint16_t* cu = smem + st * STAGE;
+        f32x16 sa[NQB], sb[NQB];
+        bf16x8 pb[NQB][2];
+        qk_sub(cu, 0, sa);
+        qk_sub(cu, 1, sb);
+        softmax_fast(sa, pb);
+        pv_sub(cu, 0, pb);
+        softmax_fast(sb, pb);
+        pv_sub(cu, 1, pb);
+        lstore(smem + (st ^ 1) * STAGE);
+        fetch(i + 2);
+        __syncthreads();
+        st ^= 1;
+      }
+#pragma unroll 1
+      for (int i = nf; i < nt; ++i) {
+        slow_tile(smem + st * STAGE, i);
+        lstore(smem + (st ^ 1) * STAGE);
+        fetch(i + 2);
+        __syncthreads();
+        st ^= 1;
+      }
+    }
+    finish();
+  } else {
+    // ---- persistent DMA-fed walk.  The workgroup takes items round by
+    // round, in snake order (within its XCD when pairs_per_xcd > 0), so
+    // every workgroup gets a similar mix of heavy and light query tiles.
+    // One DMA stream runs over the tiles of all its items: stage s % 4 holds
+    // stream tile s, filled three tiles ahead, so the first tiles of the
+    // next item load while the current one finishes.
+    const int GR = gridDim.x, wg = blockIdx.x;
+    auto item_of = [&](int r) -> int {
+      if (a.pairs_per_xcd > 0) {
+        const int NL = GR >> 3, wl = wg >> 3;
+        const int i = r * NL + ((r & 1) ? NL - 1 - wl : wl);
+        return i < (a.n_items >> 3) ? i * 8 + (wg & 7) : -1;
+      }
+      const int i = r * GR + ((r & 1) ? GR - 1 - wg : wg);
+      return i < a.n_items ? i : -1;
+    };
+    // prefetch cursor: tile c_j of item round c_r (geometry cg)
+    Geom cg{};
+    int c_r = -1, c_j = 0;
+    bool c_live = true;
+    auto c_next_item = [&]() {
+      for (;;) {
+        const int idx = item_of(++c_r);
+        if (idx < 0) {
+          c_live = false;
+          return;
+        }
+        geom(idx, cg);
+        c_j = 0;
+        if (cg.nt > 0) return;
+      }
+    };
+    c_next_item();
+    auto c_issue = [&](uint16_t* st) {
+      if (!c_live) return;
+      dma(cg, c_j, st);
+      if (++c_j == cg.nt) c_next_item();
+    };
+    int sp = 0;   // stream position of the current item's first tile
+    auto stg = [&](int i) { return smem + ((sp + i) & 3) * STAGE; };
+    c_issue(stg(0));
+    c_issue(stg(1));
+    c_issue(stg(2));
     drain();
-    f32x16 sa[NQB], sb[NQB];
-    if (nf > 0) qk_sub(smem, 0, sa);
 #pragma unroll 1
-    for (int i = 0; i < nf; ++i) {
-      const uint16_t* cur = smem + (i & 3) * STAGE;
-      dma(i + 3, smem + ((i + 3) & 3) * STAGE);
-      bf16x8 pb[NQB][2];
-      qk_sub(cur, 1, sb);
-      softmax_fast(sa, pb);
-      pin(pb);
-      pv_sub(cur, 0, pb);
-      qk_sub(smem + ((i + 1) & 3) * STAGE, 0, sa);
-      softmax_fast(sb, pb);
-      pin(pb);
-      pv_sub(cur, 1, pb);
-      settle();
-    }
+    for (int r = 0;; ++r) {
+      const int idx = item_of(r);
+      if (idx < 0) break;
+      begin_item(idx);
+      reset_acc();
+      const int nf = cur.nf, nt = cur.nt;
+      if (nt > 0) {
+        // Per fast tile: the MFMAs of the next subtile's scores are issued
+        // with the softmax of the current one; the scores of subtile 0 of
+        // the stream tile after the last fast one are computed and dropped,
+        // so the fast body has no branch besides the rare rescale.
+        f32x16 sa[NQB], sb[NQB];
+        if (nf > 0) qk_sub(stg(0), 0, sa);
 #pragma unroll 1
-    for (int i = nf; i < nt; ++i) {
-      dma(i + 3, smem + ((i + 3) & 3) * STAGE);
-      slow_tile(smem + (i & 3) * STAGE, i);
-      settle();
-    }
-    drain();   // the last prefetches (repeats of the last tile) land before exit
-  }
-
-  // ---- epilogue: lane (ql, hb) holds d = 32*dt + 8*(i/4) + 4*hb + (i%4)
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const float l_tot = half_sum(l_run[qb]);
-    if (!valid[qb]) continue;
-    if (a.n_splits == 1) {
-      const float inv = 1.f / l_tot;
-      uint16_t* op = a.out + ((size_t)(b * a.Hq + head[qb]) * a.Sq + qrow[qb]) * D + 4 * hb;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          u32x2 pk;
-          pk[0] = pack_bf16x2(o[qb][dt][4 * i4] * inv, o[qb][dt][4 * i4 + 1] * inv);
-          pk[1] = pack_bf16x2(o[qb][dt][4 * i4 + 2] * inv, o[qb][dt][4 * i4 + 3] * inv);
-          *(u32x2*)(op + 32 * dt + 8 * i4) = pk;
+        for (int i = 0; i < nf; ++i) {
+          const uint16_t* cu = stg(i);
+          c_issue(stg(i + 3));
+          bf16x8 pb[NQB][2];
+          qk_sub(cu, 1, sb);
+          softmax_fast(sa, pb);
+          pin(pb);
+          pv_sub(cu, 0, pb);
+          qk_sub(stg(i + 1), 0, sa);
+          softmax_fast(sb, pb);
+          pin(pb);
+          pv_sub(cu, 1, pb);
+          settle();
         }
-      }
-    } else {
-      const size_t rows = (size_t)a.B * a.Hq * a.n;
-      const size_t row = (size_t)(b * a.Hq + head[qb]) * a.n + qrow[qb];
-      float* po = a.part_o + ((size_t)split * rows + row) * D + 4 * hb;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          f32x4 x{o[qb][dt][4 * i4], o[qb][dt][4 * i4 + 1], o[qb][dt][4 * i4 + 2], o[qb][dt][4 * i4 + 3]};
-          *(f32x4*)(po + 32 * dt + 8 * i4) = x;
+#pragma unroll 1
+        for (int i = nf; i < nt; ++i) {
+          c_issue(stg(i + 3));
+          slow_tile(stg(i), i);
+          settle();
         }
+        sp += nt;
       }
-      if (hb == 0) {
-        float* pm = a.part_ml + ((size_t)split * rows + row) * 2;
-        pm[0] = m_run[qb] == -INFINITY ? -INFINITY : m_run[qb] * sl2;
-        pm[1] = l_tot;
-      }
+      finish();
     }
+    drain();   // the last loads and stores land before exit
   }
 }
 
@@ -715,9 +783,32 @@ static hipError_t launch_main(const AttnArgs& a, long long grid, hipStream_t st)
   return hipGetLastError();
 }
 
+// Compute units of the current device (the persistent grid size).
+static int device_cus() {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 template <int D>
-static hipError_t launch_d(const AttnPlan& p, const AttnArgs& a, hipStream_t st) {
-  hipError_t e = p.nw == 8 ? launch_main<D, 8, 32, 4>(a, p.grid, st) : launch_main<D, 4, 32, 2>(a, p.grid, st);
+static hipError_t launch_d(const AttnPlan& p, AttnArgs a, hipStream_t st) {
+  hipError_t e;
+  if (p.nw == 8) {
+    // persistent: as many workgroups as fit at once (by LDS: one per compute
+    // unit at d = 128, two below) walk their shares of the items
+    const long long slots = (long long)device_cus() * (D == 128 ? 1 : 2);
+    long long grid = p.grid < slots ? p.grid : slots;
+    if (a.pairs_per_xcd > 0 && grid % 8 != 0) a.pairs_per_xcd = 0;
+    e = launch_main<D, 8, 32, 4>(a, grid, st);
+  } else {
+    e = launch_main<D, 4, 32, 2>(a, p.grid, st);
+  }
   if (e != hipSuccess || p.n_splits == 1) return e;
   const long long rows = (long long)p.B * p.Hq * p.n;
   const long long threads = rows * (D / 4);
@@ -754,6 +845,7 @@ hipError_t attn_launch(const AttnPlan& p, const void* q, const void* k, const vo
   a.n_splits = p.n_splits;
   a.split_keys = p.split_keys;
   a.pairs_per_xcd = p.pairs_per_xcd;
+  a.n_items = (int)p.grid;
   a.sl2 = 1.4426950408889634f / sqrtf((float)p.d);
   (void)hipGetLastError();
   switch (p.d) {
