@@ -254,6 +254,50 @@ def secondary(bda, synth, torch, dev, args):
         del sets, out, ws
         torch.cuda.empty_cache()
 
+    # ---- multimodal prefill: causal over the 4096-token prefix, B=2
+    case = synth.multimodal_prefill()
+    B, Hq, n, d = case.q.shape
+    L = case.L
+    fl = 4 * d * causal_pairs(L, n) * B * Hq
+    q, k, v = case.q.to(dev), case.k.to(dev), case.v.to(dev)
+    out = torch.empty_like(q)
+    mean, med = time_launches(lambda i: bda.attn_fwd(q, k, v, "causal", n, out=out), iters, 5)
+    res["prefill_attention"] = {"B": B, "n": n, "kv_len": L, "us_per_call": round(mean * 1e3, 2),
+                                "TFLOP/s": round(fl / (mean * 1e-3) / 1e12, 2),
+                                "mfma_frac": round(fl / (mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    log(f"[bench] prefill_attention: {res['prefill_attention']}")
+    del q, k, v, out
+    torch.cuda.empty_cache()
+
+    # ---- one canvas denoise step mid-canvas: decode attention of the 28-row
+    # block over prefix + four finished blocks, then the commit (threshold
+    # 0.9) on its [2, 28, 131072] logits.  Both are launch-latency bound; the
+    # floors are their HBM bytes at 8 TB/s (the cache also fits the 256 MB
+    # last-level cache, as it would between real steps).
+    qs, kb, vb, lg, _ = synth.multimodal_step(0, 28)
+    pre_k = torch.randn(2, 8, synth.PREFIX + 4 * 28, 128, generator=torch.Generator().manual_seed(9)).to(torch.bfloat16)
+    k = torch.cat([pre_k, kb], dim=2).to(dev)
+    v = torch.cat([pre_k.flip(2), vb], dim=2).to(dev)
+    qs, lg = qs.to(dev), lg.to(dev)
+    L = k.shape[2]
+    out = torch.empty_like(qs)
+    ws = torch.empty(max(1, bda.attn_workspace_bytes(2, 32, 8, L, 128, 28, "decode")), dtype=torch.uint8, device=dev)
+    t_att, _ = time_launches(lambda i: bda.attn_fwd(qs, k, v, "decode", 28, out=out, workspace=ws), iters, 5)
+    tok = torch.full((2, 28), -1, dtype=torch.int64, device=dev)
+    msk = torch.ones(2, 28, dtype=torch.uint8, device=dev)
+    cws = torch.empty(bda.lib.bda_commit_workspace_bytes(2, 28, synth.VOCAB), dtype=torch.uint8, device=dev)
+    t_com, _ = time_launches(lambda i: bda.commit(lg, tok, msk, 0.9, 1, workspace=cws), iters, 5,
+                             pre=lambda i: msk.fill_(1))
+    att_bytes = (qs.numel() * 2 * 2) + k.numel() * 2 * 2
+    com_bytes = lg.numel() * 2
+    res["canvas_step"] = {"B": 2, "n": 28, "kv_len": L, "attention_us": round(t_att * 1e3, 2),
+                          "attention_floor_us": round(att_bytes / PEAK_HBM_GBS / 1e3, 2),
+                          "commit_us": round(t_com * 1e3, 2),
+                          "commit_floor_us": round(com_bytes / PEAK_HBM_GBS / 1e3, 2)}
+    log(f"[bench] canvas_step: {res['canvas_step']}")
+    del k, v, qs, lg, out, ws, cws
+    torch.cuda.empty_cache()
+
     # ---- commit on decode-form logits [32, 28, 131072] bf16, threshold 0.85
     logits, idx, masked0 = synth.commit_logits()
     G, R, V = logits.shape

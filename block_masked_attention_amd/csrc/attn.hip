@@ -728,6 +728,7 @@ int attn_make_plan(int B, int Hq, int Hkv, int L, int d, int block, int mode, At
     x.n = 2 * L;
     x.Sq = x.Sk = 2 * L;
     x.nw = L >= 256 ? 8 : 4;
+    x.stages = L >= 256 ? 4 : 2;
     x.qpw = 32;
     const int slots_half = (x.nw / 2) * x.qpw;
     if (x.G > slots_half) {
@@ -741,6 +742,7 @@ int attn_make_plan(int B, int Hq, int Hkv, int L, int d, int block, int mode, At
     x.Sq = block;
     x.Sk = L;
     x.nw = block >= 128 ? 8 : 4;
+    x.stages = block >= 128 ? 4 : 2;
     x.qpw = 32;
     const int slots = x.nw * x.qpw;
     if (x.G > slots) {
@@ -750,9 +752,10 @@ int attn_make_plan(int B, int Hq, int Hkv, int L, int d, int block, int mode, At
     x.rows_per_wg = slots / x.G;
     x.n_qtiles = (block + x.rows_per_wg - 1) / x.rows_per_wg;
     // Split the keys when (batch x kv head x query tile) alone cannot keep
-    // every CU streaming; each split keeps at least 4 key tiles.
+    // every CU streaming (two resident 4-wave workgroups per CU); each split
+    // keeps at least 4 key tiles.
     const long long items = (long long)B * Hkv * x.n_qtiles;
-    const long long target = 512;      // two resident workgroups per CU
+    const long long target = 512;
     int splits = (int)((target + items - 1) / items);
     const int max_splits = (L + 4 * kBN - 1) / (4 * kBN);
     if (splits > max_splits) splits = max_splits;
@@ -799,7 +802,7 @@ static int device_cus() {
 template <int D>
 static hipError_t launch_d(const AttnPlan& p, AttnArgs a, hipStream_t st) {
   hipError_t e;
-  if (p.nw == 8) {
+  if (p.stages == 4) {
     // persistent: as many workgroups as fit at once (by LDS: one per compute
     // unit at d = 128, two below) walk their shares of the items
     const long long slots = (long long)device_cus() * (D == 128 ? 1 : 2);

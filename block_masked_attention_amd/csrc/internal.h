@@ -13,6 +13,7 @@ struct AttnPlan {
   int mode, B, Hq, Hkv, G, L, n, blk, d;
   int Sq, Sk;           // rows of the query / key tensors
   int nw;               // wavefronts per workgroup
+  int stages;           // 4: persistent DMA-fed walk; 2: one item per workgroup
   int qpw;              // query slots per wavefront (32 or 64)
   int rows_per_wg;      // query rows per workgroup (per half in HYBRID)
   int n_qtiles;         // query tiles per (batch, kv head)

@@ -14,6 +14,8 @@ import torch
 
 import oracle
 import synth
+from commit_util import close_rows as _close_rows
+from commit_util import guarded as _guarded
 from gpu_util import GUARD, dev, say
 
 pytestmark = pytest.mark.gpu
@@ -27,36 +29,6 @@ def _gpu_commit(logits, masked, tokens, tau, k_min):
     bda.commit(logits.to(dev()), t, m, tau, k_min)
     torch.cuda.synchronize()
     return t.cpu(), m.cpu()
-
-
-def _close_rows(info, masked, tau, k_min):
-    """Rows whose decision lies inside the guard band (from the oracle)."""
-    p = info["p64"]
-    G, R = p.shape
-    bad = set()
-    for g in range(G):
-        rows = [r for r in range(R) if masked[g, r]]
-        for r in rows:
-            if abs(p[g, r] - tau) <= GUARD:
-                bad.add((g, r))
-        below = sorted((r for r in rows if np.float32(p[g, r]) <= np.float32(tau)),
-                       key=lambda r: (-float(np.float32(p[g, r])), r))
-        need = min(k_min, len(rows)) - (len(rows) - len(below))
-        if 0 < need < len(below) and p[g, below[need - 1]] - p[g, below[need]] <= GUARD:
-            bad.update({(g, below[need - 1]), (g, below[need])})
-    return sorted(bad)
-
-
-def _guarded(logits, idx, masked, tau, k_min, sigma, seed):
-    for it in range(8):
-        tokens = torch.full(masked.shape, -1, dtype=torch.int64)
-        _, _, info = oracle.commit(logits, masked.numpy(), tokens.numpy(), tau, k_min)
-        bad = _close_rows(info, masked.numpy(), tau, k_min)
-        if not bad:
-            return logits, info
-        say(f"  redrawing {len(bad)} rows inside the guard band")
-        synth.redraw_rows(logits, idx, bad, seed=seed * 100 + it, sigma=sigma)
-    raise AssertionError("could not leave the guard band")
 
 
 def _check(logits, masked, tau, k_min, what):
