@@ -329,6 +329,15 @@ def secondary(bda, synth, torch, dev, args):
     if not args.no_cpu:
         res["commit"]["cpu_baseline"] = cpu_baseline_commit(logits, masked0, 0.85, 1)
 
+    # ---- row statistics (confidence, argmax, entropy) on the same logits
+    sws = torch.empty(bda.lib.bda_row_stats_workspace_bytes(G, R, V), dtype=torch.uint8, device=dev)
+    mean, med = time_launches(lambda i: bda.row_stats(sets[i % 3], workspace=sws), iters, 5)
+    res["row_stats"] = {"G": G, "R": R, "V": V, "us_per_call": round(mean * 1e3, 2),
+                        "GB/s": round(byts / (mean * 1e-3) / 1e9, 1),
+                        "hbm_frac": round(byts / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                        "algorithmic_bytes": byts}
+    log(f"[bench] row_stats: {res['row_stats']}")
+
     # ---- verify on [16, 28, 131072] bf16
     vl, vidx, _ = synth.commit_logits(seed=6, G=16, R=28)
     drafts, _ = synth.verify_drafts(vidx)

@@ -24,7 +24,7 @@ TILE_FULL, TILE_EMPTY, TILE_PARTIAL = 0, 1, 2
 _ENTRY_POINTS = (
     "bda_attn_fwd", "bda_attn_workspace_bytes", "bda_commit", "bda_commit_workspace_bytes",
     "bda_verify", "bda_verify_workspace_bytes", "bda_classify_tile", "bda_strerror",
-    "bda_last_error", "bda_version",
+    "bda_last_error", "bda_version", "bda_row_stats", "bda_row_stats_workspace_bytes",
 )
 
 
@@ -52,6 +52,10 @@ def _load():
     L.bda_verify.restype = I
     L.bda_verify_workspace_bytes.argtypes = [I, I, I]
     L.bda_verify_workspace_bytes.restype = S
+    L.bda_row_stats.argtypes = [P, I, P, P, P, P, P, I, I, I, P, S, P]
+    L.bda_row_stats.restype = I
+    L.bda_row_stats_workspace_bytes.argtypes = [I, I, I]
+    L.bda_row_stats_workspace_bytes.restype = S
     L.bda_classify_tile.argtypes = [I, I, I, I, I, I, I]
     L.bda_classify_tile.restype = I
     for name in ("bda_strerror",):
@@ -179,6 +183,34 @@ def verify(logits, drafts, workspace=None):
     if rc:
         raise BdaError(rc, "bda_verify")
     return am, acc
+
+
+def row_stats(logits, masked=None, workspace=None):
+    """Per-row softmax statistics of logits [G,R,V] (bf16 or fp32): returns
+    (conf [G,R] float32, argmax [G,R] int64, entropy [G,R] float32 in nats,
+    mean_entropy [G] float32).  With ``masked`` (uint8 [G,R]) only rows with
+    masked != 0 are computed; the other rows' outputs are NaN / -1 and the
+    group means cover the computed rows only."""
+    if logits.dim() != 3:
+        raise ValueError("logits must be [G, R, V]")
+    G, R, V = logits.shape
+    dt = {torch.bfloat16: BF16, torch.float32: F32}.get(logits.dtype)
+    if dt is None:
+        raise ValueError("logits must be bfloat16 or float32")
+    if masked is not None and (masked.dtype != torch.uint8 or tuple(masked.shape) != (G, R)):
+        raise ValueError("masked must be uint8 [G, R]")
+    dev = _check_dev(logits, masked)
+    conf = torch.full((G, R), float("nan"), dtype=torch.float32, device=dev)
+    am = torch.full((G, R), -1, dtype=torch.int64, device=dev)
+    ent = torch.full((G, R), float("nan"), dtype=torch.float32, device=dev)
+    mean = torch.empty(G, dtype=torch.float32, device=dev)
+    need = int(lib.bda_row_stats_workspace_bytes(G, R, V))
+    ws = _workspace(need, dev, workspace)
+    rc = lib.bda_row_stats(_ptr(logits), dt, _ptr(masked), _ptr(conf), _ptr(am), _ptr(ent), _ptr(mean),
+                           G, R, V, _ptr(ws), need, _stream(dev))
+    if rc:
+        raise BdaError(rc, "bda_row_stats")
+    return conf, am, ent, mean
 
 
 def classify_tile(mode, L, block, q0, q1, k0, k1) -> int:

@@ -172,6 +172,39 @@ int bda_verify(const void* logits, int dtype, const int64_t* drafts, int64_t* ar
   return ok();
 }
 
+size_t bda_row_stats_workspace_bytes(int G, int R, int V) { return bda_commit_workspace_bytes(G, R, V); }
+
+int bda_row_stats(const void* logits, int dtype, const uint8_t* masked, float* conf, int64_t* argmax_out,
+                  float* entropy, float* mean_entropy, int G, int R, int V, void* workspace,
+                  size_t ws_bytes, void* stream) {
+  if (int e = check_logits(logits, dtype, G, R, V, "G")) return e;
+  if (G == 0) return ok();
+  const size_t rows = (size_t)G * R;
+  const size_t lbytes = rows * V * (dtype == BDA_BF16 ? 2 : 4);
+  if (rows && ((conf && overlap(conf, rows * 4, logits, lbytes)) ||
+               (argmax_out && overlap(argmax_out, rows * 8, logits, lbytes)) ||
+               (entropy && overlap(entropy, rows * 4, logits, lbytes)) ||
+               (conf && argmax_out && overlap(conf, rows * 4, argmax_out, rows * 8)) ||
+               (conf && entropy && overlap(conf, rows * 4, entropy, rows * 4)) ||
+               (entropy && argmax_out && overlap(entropy, rows * 4, argmax_out, rows * 8))))
+    return fail(BDA_EINVAL, "outputs must not overlap the logits or each other");
+  if (mean_entropy && (overlap(mean_entropy, (size_t)G * 4, logits, lbytes) ||
+                       (conf && overlap(mean_entropy, (size_t)G * 4, conf, rows * 4)) ||
+                       (entropy && overlap(mean_entropy, (size_t)G * 4, entropy, rows * 4)) ||
+                       (argmax_out && overlap(mean_entropy, (size_t)G * 4, argmax_out, rows * 8))))
+    return fail(BDA_EINVAL, "mean_entropy must not overlap the logits or other outputs");
+  bda::CommitPlan p;
+  bda::commit_make_plan(G, R, V, dtype, &p);
+  if (!workspace || ws_bytes < p.ws_bytes)
+    return fail(BDA_EWORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_bytes,
+                workspace ? ws_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(BDA_EINVAL, "workspace must be 16-byte aligned");
+  hipError_t e = bda::stats_launch(p, logits, masked, conf, argmax_out, entropy, mean_entropy, workspace,
+                                   (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BDA_EHIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int bda_classify_tile(int mode, int L, int block, int q0, int q1, int k0, int k1) {
   if (mode < 0 || mode > 2 || L < 1 || block < 1 || block > L) return -1;
   const int rows = mode == BDA_MODE_HYBRID ? 2 * L : block;

@@ -17,6 +17,12 @@
 // Pass 2 (finalize): one workgroup per group merges the chunk partials of
 // its rows in chunk order, takes p = 1/Z, applies the threshold and the
 // minimum-count fallback, and writes tokens / masked.
+//
+// Row statistics (entropy for adaptive stopping and entropy-bound commits,
+// "Adaptive stopping" and "Schedulers" of the DiffusionGemma pipeline page)
+// add T = sum exp(l - m) (l - m) to the same stream; the merge rule is
+// T = sum_i e^(m_i-m) (T_i + (m_i - m) Z_i), and the entropy in nats is
+// H = log Z - T / Z.
 #include <limits.h>
 
 #include "common.h"
@@ -28,28 +34,35 @@ constexpr int kCommitThreads = 256;
 constexpr int kChunk = 16384;            // vocabulary entries per streaming workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 
+// What the stream accumulates: the argmax only, also Z, or also Z and T.
+enum { kArgmax = 0, kWithZ = 1, kWithZT = 2 };
+
 struct Partial {
   float m, z;
-  int a, pad;
+  int a;
+  float t;
 };
 
 struct Stat {
   float m, z;
   int a;
+  float t;
 };
 
-__device__ __forceinline__ Stat merge(Stat x, Stat y, bool with_z) {
+__device__ __forceinline__ Stat merge(Stat x, Stat y, int kind) {
   Stat r;
   r.m = fmaxf(x.m, y.m);
   r.a = x.m > y.m ? x.a : (y.m > x.m ? y.a : min(x.a, y.a));
-  if (with_z) {
-    if (r.m == -INFINITY) {
-      r.z = 0.f;
-    } else {
-      r.z = x.z * exp2_fast((x.m - r.m) * kLog2e) + y.z * exp2_fast((y.m - r.m) * kLog2e);
-    }
-  } else {
-    r.z = 0.f;
+  r.z = 0.f;
+  r.t = 0.f;
+  if (kind != kArgmax && r.m != -INFINITY) {
+    // a side whose maximum is -inf holds no value and contributes nothing
+    const float dx = x.m - r.m, dy = y.m - r.m;
+    const float ax = x.m == -INFINITY ? 0.f : exp2_fast(dx * kLog2e);
+    const float ay = y.m == -INFINITY ? 0.f : exp2_fast(dy * kLog2e);
+    r.z = x.z * ax + y.z * ay;
+    if (kind == kWithZT)
+      r.t = (x.m == -INFINITY ? 0.f : ax * (x.t + dx * x.z)) + (y.m == -INFINITY ? 0.f : ay * (y.t + dy * y.z));
   }
   return r;
 }
@@ -61,7 +74,7 @@ __device__ __forceinline__ float load_one(const void* row, int j) {
 }
 
 // Fold 8 values (indices base..base+7, increasing) into a lane's state.
-template <bool WITH_Z>
+template <int KIND>
 __device__ __forceinline__ void fold8(Stat& s, const float (&x)[8], int base) {
   float lm = x[0];
 #pragma unroll
@@ -70,20 +83,34 @@ __device__ __forceinline__ void fold8(Stat& s, const float (&x)[8], int base) {
     int idx = 7;
 #pragma unroll
     for (int e = 6; e >= 0; --e) idx = x[e] == lm ? e : idx;
-    if (WITH_Z) s.z = s.m == -INFINITY ? 0.f : s.z * exp2_fast((s.m - lm) * kLog2e);
+    if (KIND != kArgmax) {
+      if (s.m == -INFINITY) {
+        s.z = 0.f;
+        s.t = 0.f;
+      } else {
+        const float d = s.m - lm, a = exp2_fast(d * kLog2e);
+        if (KIND == kWithZT) s.t = a * (s.t + d * s.z);
+        s.z *= a;
+      }
+    }
     s.m = lm;
     s.a = base + idx;
   }
-  if (WITH_Z && s.m != -INFINITY) {
+  if (KIND != kArgmax && s.m != -INFINITY) {
     const float nb = -s.m * kLog2e;
-    float acc = 0.f;
+    float acc = 0.f, acct = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc += exp2_fast(fmaf(x[e], kLog2e, nb));
+    for (int e = 0; e < 8; ++e) {
+      const float p = exp2_fast(fmaf(x[e], kLog2e, nb));
+      acc += p;
+      if (KIND == kWithZT) acct = fmaf(p, x[e] == -INFINITY ? 0.f : x[e] - s.m, acct);   // -inf: padding
+    }
     s.z += acc;
+    if (KIND == kWithZT) s.t += acct;
   }
 }
 
-template <bool BF16, bool WITH_Z>
+template <bool BF16, int KIND>
 __global__ __launch_bounds__(kCommitThreads) void stream_kernel(const void* __restrict__ logits,
                                                                 const uint8_t* __restrict__ masked,
                                                                 Partial* __restrict__ part, int V,
@@ -99,7 +126,7 @@ __global__ __launch_bounds__(kCommitThreads) void stream_kernel(const void* __re
   const int c0 = c * kChunk;
   const int c1 = min(V, c0 + kChunk);
 
-  Stat s{-INFINITY, 0.f, INT_MAX};
+  Stat s{-INFINITY, 0.f, INT_MAX, 0.f};
   if (vec_ok && c1 - c0 == kChunk) {
     // Whole chunk: every load of the thread is issued before any arithmetic
     // (vector v covers values c0 + 8*(v*256 + tid) + 0..7, so a wavefront
@@ -144,15 +171,20 @@ __global__ __launch_bounds__(kCommitThreads) void stream_kernel(const void* __re
         s.a = c0 + 8 * (v * kCommitThreads + tid) + idx;
       }
     }
-    // pass 2: Z against that maximum
-    if (WITH_Z) {
+    // pass 2: Z (and T) against that maximum
+    if (KIND != kArgmax) {
       const float nb = -s.m * kLog2e;
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      float acc[4] = {0.f, 0.f, 0.f, 0.f}, acct[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int v = 0; v < VPT; ++v)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e & 3] += exp2_fast(fmaf(x[v][e], kLog2e, nb));
+        for (int e = 0; e < 8; ++e) {
+          const float p = exp2_fast(fmaf(x[v][e], kLog2e, nb));
+          acc[e & 3] += p;
+          if (KIND == kWithZT) acct[e & 3] = fmaf(p, x[v][e] - s.m, acct[e & 3]);
+        }
       s.z = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      s.t = (acct[0] + acct[1]) + (acct[2] + acct[3]);
     }
   } else if (vec_ok) {
     // 8 consecutive values per step: one 16-byte load (bf16) or two (fp32).
@@ -179,14 +211,14 @@ __global__ __launch_bounds__(kCommitThreads) void stream_kernel(const void* __re
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = base + e < c1 ? load_one<BF16>(row, base + e) : -INFINITY;
       }
-      fold8<WITH_Z>(s, x, base);
+      fold8<KIND>(s, x, base);
     }
   } else {
     for (int base = c0 + 8 * tid; base < c1; base += 8 * kCommitThreads) {
       float x[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = base + e < c1 ? load_one<BF16>(row, base + e) : -INFINITY;
-      fold8<WITH_Z>(s, x, base);
+      fold8<KIND>(s, x, base);
     }
   }
   // -INFINITY padding never wins a strict comparison, and contributes 0 to Z
@@ -198,7 +230,8 @@ __global__ __launch_bounds__(kCommitThreads) void stream_kernel(const void* __re
     o.m = __shfl_xor(s.m, off);
     o.z = __shfl_xor(s.z, off);
     o.a = __shfl_xor(s.a, off);
-    s = merge(s, o, WITH_Z);
+    o.t = __shfl_xor(s.t, off);
+    s = merge(s, o, KIND);
   }
   __shared__ Stat wst[kCommitThreads / 64];
   if ((tid & 63) == 0) wst[tid >> 6] = s;
@@ -206,21 +239,22 @@ __global__ __launch_bounds__(kCommitThreads) void stream_kernel(const void* __re
   if (tid == 0) {
     Stat r = wst[0];
 #pragma unroll
-    for (int w = 1; w < kCommitThreads / 64; ++w) r = merge(r, wst[w], WITH_Z);
+    for (int w = 1; w < kCommitThreads / 64; ++w) r = merge(r, wst[w], KIND);
     Partial p;
     p.m = r.m;
     p.z = r.z;
     p.a = r.a;
-    p.pad = 0;
+    p.t = r.t;
     part[(size_t)t * n_chunks + c] = p;
   }
 }
 
-__device__ __forceinline__ Stat row_stat(const Partial* part, size_t t, int n_chunks, bool with_z) {
-  Stat s{part[t * n_chunks].m, part[t * n_chunks].z, part[t * n_chunks].a};
+__device__ __forceinline__ Stat row_stat(const Partial* part, size_t t, int n_chunks, int kind) {
+  const Partial& q0 = part[t * n_chunks];
+  Stat s{q0.m, q0.z, q0.a, q0.t};
   for (int c = 1; c < n_chunks; ++c) {
     const Partial& q = part[t * n_chunks + c];
-    s = merge(s, Stat{q.m, q.z, q.a}, with_z);
+    s = merge(s, Stat{q.m, q.z, q.a, q.t}, kind);
   }
   return s;
 }
@@ -250,7 +284,7 @@ __global__ __launch_bounds__(kCommitThreads) void commit_finalize_kernel(
     const size_t t = base + r;
     uint8_t f = 0;
     if (masked[t]) {
-      const Stat s = row_stat(part, t, n_chunks, true);
+      const Stat s = row_stat(part, t, n_chunks, kWithZ);
       const float p = 1.f / s.z;
       rowp[t] = p;
       rowa[t] = s.a;
@@ -295,7 +329,7 @@ __global__ __launch_bounds__(kCommitThreads) void verify_finalize_kernel(
   int first = R;
   for (int r = threadIdx.x; r < R; r += kCommitThreads) {
     const size_t t = (size_t)b * R + r;
-    const Stat s = row_stat(part, t, n_chunks, false);
+    const Stat s = row_stat(part, t, n_chunks, kArgmax);
     argmax_out[t] = s.a;
     if ((int64_t)s.a != drafts[t]) first = min(first, r);
   }
@@ -308,6 +342,46 @@ __global__ __launch_bounds__(kCommitThreads) void verify_finalize_kernel(
     for (int w = 1; w < kCommitThreads / 64; ++w) m = min(m, red[w]);
     accept[b] = m;
   }
+}
+
+__device__ __forceinline__ float block_sum_f(float x, float* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int w = 0; w < kCommitThreads / 64; ++w) s += red[w];
+  __syncthreads();
+  return s;
+}
+
+// One workgroup per group: per selected row the confidence 1/Z, the argmax
+// and the entropy log Z - T/Z (nats); the group's mean entropy over its
+// selected rows (0 when none is selected).
+__global__ __launch_bounds__(kCommitThreads) void stats_finalize_kernel(
+    const Partial* __restrict__ part, int n_chunks, const uint8_t* __restrict__ masked, int R,
+    float* __restrict__ conf, int64_t* __restrict__ argmax_out, float* __restrict__ entropy,
+    float* __restrict__ mean_entropy) {
+  __shared__ float redf[kCommitThreads / 64];
+  __shared__ int redi[kCommitThreads / 64];
+  const int g = blockIdx.x;
+  float hsum = 0.f;
+  int cnt = 0;
+  for (int r = threadIdx.x; r < R; r += kCommitThreads) {
+    const size_t t = (size_t)g * R + r;
+    if (masked != nullptr && masked[t] == 0) continue;
+    const Stat s = row_stat(part, t, n_chunks, kWithZT);
+    const float h = logf(s.z) - s.t / s.z;
+    if (conf) conf[t] = 1.f / s.z;
+    if (argmax_out) argmax_out[t] = s.a;
+    if (entropy) entropy[t] = h;
+    hsum += h;
+    cnt += 1;
+  }
+  hsum = block_sum_f(hsum, redf);
+  cnt = block_sum(cnt, redi);
+  if (threadIdx.x == 0 && mean_entropy) mean_entropy[g] = cnt > 0 ? hsum / (float)cnt : 0.f;
 }
 
 // ----------------------------------------------------------------------------
@@ -346,16 +420,16 @@ static bool vec_ok(const void* logits, int V, int dtype) {
   return ((uintptr_t)logits % 16) == 0 && V % per16 == 0;
 }
 
-template <bool WITH_Z>
+template <int KIND>
 static hipError_t launch_stream(const CommitPlan& p, const void* logits, const uint8_t* masked,
                                 Partial* part, hipStream_t st) {
   const long long grid = (long long)p.G * p.R * p.n_chunks;
   const int vo = vec_ok(logits, p.V, p.dtype);
   if (p.dtype == 0)
-    hipLaunchKernelGGL((stream_kernel<true, WITH_Z>), dim3((unsigned)grid), dim3(kCommitThreads), 0,
+    hipLaunchKernelGGL((stream_kernel<true, KIND>), dim3((unsigned)grid), dim3(kCommitThreads), 0,
                        st, logits, masked, part, p.V, p.n_chunks, vo);
   else
-    hipLaunchKernelGGL((stream_kernel<false, WITH_Z>), dim3((unsigned)grid), dim3(kCommitThreads), 0,
+    hipLaunchKernelGGL((stream_kernel<false, KIND>), dim3((unsigned)grid), dim3(kCommitThreads), 0,
                        st, logits, masked, part, p.V, p.n_chunks, vo);
   return hipGetLastError();
 }
@@ -369,7 +443,7 @@ hipError_t commit_launch(const CommitPlan& p, const void* logits, int64_t* token
   uint8_t* rowf;
   carve(p, ws, &part, &rowp, &rowa, &rowf);
   (void)hipGetLastError();
-  hipError_t e = launch_stream<true>(p, logits, masked, part, st);
+  hipError_t e = launch_stream<kWithZ>(p, logits, masked, part, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(commit_finalize_kernel, dim3(p.G), dim3(kCommitThreads), 0, st, part,
                      p.n_chunks, tokens, masked, threshold, k_min, p.R, rowp, rowa, rowf);
@@ -386,11 +460,30 @@ hipError_t verify_launch(const CommitPlan& p, const void* logits, const int64_t*
   carve(p, ws, &part, &rowp, &rowa, &rowf);
   (void)hipGetLastError();
   if (p.R > 0) {
-    hipError_t e = launch_stream<false>(p, logits, nullptr, part, st);
+    hipError_t e = launch_stream<kArgmax>(p, logits, nullptr, part, st);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(verify_finalize_kernel, dim3(p.G), dim3(kCommitThreads), 0, st, part,
                      p.n_chunks, drafts, argmax_out, accept, p.R);
+  return hipGetLastError();
+}
+
+hipError_t stats_launch(const CommitPlan& p, const void* logits, const uint8_t* masked, float* conf,
+                        int64_t* argmax_out, float* entropy, float* mean_entropy, void* ws,
+                        hipStream_t st) {
+  if (p.G == 0) return hipSuccess;
+  Partial* part;
+  float* rowp;
+  int* rowa;
+  uint8_t* rowf;
+  carve(p, ws, &part, &rowp, &rowa, &rowf);
+  (void)hipGetLastError();
+  if (p.R > 0) {
+    hipError_t e = launch_stream<kWithZT>(p, logits, masked, part, st);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(stats_finalize_kernel, dim3(p.G), dim3(kCommitThreads), 0, st, part, p.n_chunks,
+                     masked, p.R, conf, argmax_out, entropy, mean_entropy);
   return hipGetLastError();
 }
 

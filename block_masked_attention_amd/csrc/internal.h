@@ -39,6 +39,9 @@ struct CommitPlan {
 int commit_make_plan(int G, int R, int V, int dtype, CommitPlan* p);
 hipError_t commit_launch(const CommitPlan& p, const void* logits, int64_t* tokens, uint8_t* masked,
                          float threshold, int k_min, void* ws, hipStream_t st);
+hipError_t stats_launch(const CommitPlan& p, const void* logits, const uint8_t* masked, float* conf,
+                        int64_t* argmax_out, float* entropy, float* mean_entropy, void* ws,
+                        hipStream_t st);
 hipError_t verify_launch(const CommitPlan& p, const void* logits, const int64_t* drafts,
                          int64_t* argmax_out, int32_t* accept, void* ws, hipStream_t st);
 

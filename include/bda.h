@@ -117,6 +117,28 @@ int bda_verify(const void* logits, int dtype, const int64_t* drafts,
 size_t bda_verify_workspace_bytes(int B, int R, int V);
 
 /*
+ * Per-row statistics of a softmax over the vocabulary, for adaptive stopping
+ * and entropy-based commits ([DGemma] adaptive stopping: freeze an example
+ * once its argmax is stable and its mean per-token entropy is below a
+ * confidence threshold; [DGemma] Schedulers: the entropy-bound scheduler
+ * commits the lowest-entropy positions) and the SPRINT confidence ([LLaDA]).
+ * logits: [G, R, V] of dtype BDA_BF16 or BDA_F32; values must be finite.
+ * masked: [G, R] uint8 or NULL.  When given, only rows with masked != 0 are
+ *   computed (outputs of the other rows are left untouched); NULL = all rows.
+ * For each computed row, with p = softmax(row) at temperature 1:
+ *   conf[g,r]    (float, [G,R]) = max p,
+ *   argmax[g,r]  (int64, [G,R]) = lowest index of the largest logit,
+ *   entropy[g,r] (float, [G,R]) = -sum p log p in nats.
+ * mean_entropy[g] (float, [G]) = mean entropy of the group's computed rows
+ *   (0 when it has none).  Any of the four outputs may be NULL (not written).
+ * workspace: at least bda_row_stats_workspace_bytes(G, R, V) bytes.
+ */
+int bda_row_stats(const void* logits, int dtype, const uint8_t* masked, float* conf,
+                  int64_t* argmax, float* entropy, float* mean_entropy, int G, int R, int V,
+                  void* workspace, size_t ws_bytes, void* stream);
+size_t bda_row_stats_workspace_bytes(int G, int R, int V);
+
+/*
  * Host-only tile classifier (the rule the attention kernels use to skip and
  * to take their unmasked fast path).  Rows [q0, q1) of the query tensor and
  * keys [k0, k1) of the key tensor, in the row numbering of bda_attn_fwd for

@@ -53,9 +53,10 @@ def _load():
     lib.oracle_attention.argtypes = [I, P, P, P, P, L, L, L, L, L, L, P, L, I]
     lib.oracle_commit.argtypes = [P, P, P, F, L, L, L, L, P, P, P, P, I]
     lib.oracle_verify.argtypes = [P, P, P, P, L, L, L, I]
+    lib.oracle_row_stats.argtypes = [P, P, P, P, P, P, L, L, L, I]
     lib.oracle_max_threads.restype = I
     for f in (lib.oracle_mask_shape, lib.oracle_mask, lib.oracle_attention,
-              lib.oracle_commit, lib.oracle_verify):
+              lib.oracle_commit, lib.oracle_verify, lib.oracle_row_stats):
         f.restype = I
     _lib = lib
     return lib
@@ -142,6 +143,24 @@ def verify(logits, drafts, nthreads: int = 0):
     if rc:
         raise ValueError("oracle_verify: bad arguments")
     return am, acc
+
+
+def row_stats(logits, masked=None, nthreads: int = 0):
+    """Per-row softmax statistics in double: (conf, argmax, entropy [nats],
+    group mean entropy).  Rows with masked == 0 are not computed (NaN / -1)."""
+    lib = _load()
+    lg = _f32(logits)
+    G, R, V = lg.shape
+    m = None if masked is None else np.ascontiguousarray(np.asarray(masked, dtype=np.uint8))
+    conf = np.full((G, R), np.nan)
+    am = np.full((G, R), -1, dtype=np.int64)
+    ent = np.full((G, R), np.nan)
+    mean = np.empty(G)
+    rc = lib.oracle_row_stats(_ptr(lg), _ptr(m), _ptr(conf), _ptr(am), _ptr(ent), _ptr(mean), G, R, V,
+                              nthreads)
+    if rc:
+        raise ValueError("oracle_row_stats: bad arguments")
+    return conf, am, ent, mean
 
 
 def tile_class(M: np.ndarray, q0: int, q1: int, k0: int, k1: int) -> int:

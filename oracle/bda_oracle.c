@@ -339,6 +339,59 @@ int oracle_verify(const float* logits, const int64_t* drafts, int64_t* argmax_ou
     return 0;
 }
 
+/*
+ * Per-row softmax statistics ([DGemma] "Adaptive stopping": the mean
+ * per-token entropy of the predicted distribution; "Schedulers": the
+ * entropy-bound scheduler ranks positions by entropy; [LLaDA] SPRINT:
+ * confidence = top-1 probability).  For each selected row (masked == NULL or
+ * masked[t] != 0): p_j = exp(l_j) / sum_k exp(l_k) at temperature 1,
+ * conf = max_j p_j, argmax = lowest j reaching the largest logit, and the
+ * entropy -sum_j p_j log p_j in nats, written term by term (p_j = 0 adds
+ * nothing).  mean[g] = mean entropy over the group's selected rows, 0 if
+ * none.  Unselected rows are left untouched.
+ */
+int oracle_row_stats(const float* logits, const uint8_t* masked, double* conf, int64_t* argmax,
+                     double* entropy, double* mean, long G, long R, long V, int nthreads)
+{
+    if (G < 0 || R < 0 || V <= 0) return 1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long t = 0; t < G * R; ++t) {
+        if (masked && !masked[t]) continue;
+        const float* row = logits + t * V;
+        double m = (double)row[0];
+        long idx = 0;
+        for (long j = 1; j < V; ++j)
+            if ((double)row[j] > m) { m = (double)row[j]; idx = j; }
+        double Z = 0.0;
+        for (long j = 0; j < V; ++j) Z += exp((double)row[j] - m);
+        double H = 0.0;
+        for (long j = 0; j < V; ++j) {
+            const double pj = exp((double)row[j] - m) / Z;
+            if (pj > 0.0) H -= pj * log(pj);
+        }
+        conf[t] = 1.0 / Z;
+        argmax[t] = idx;
+        entropy[t] = H;
+    }
+    for (long g = 0; g < G; ++g) {
+        double sum = 0.0;
+        long n = 0;
+        for (long r = 0; r < R; ++r) {
+            const long t = g * R + r;
+            if (masked && !masked[t]) continue;
+            sum += entropy[t];
+            ++n;
+        }
+        mean[g] = n > 0 ? sum / (double)n : 0.0;
+    }
+    return 0;
+}
+
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP

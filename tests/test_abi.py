@@ -108,3 +108,17 @@ def test_classifier_matches_dense_mask(mode, L, b):
                         (mode, L, b, q0, q1, k0, k1)
     assert bda.classify_tile(mode, L, b, 0, rows + 1, 0, 1) == -1
     assert bda.classify_tile(mode, L, b, 0, 1, 2, 1) == -1
+
+
+def test_row_stats_validation():
+    f = bda.lib.bda_row_stats
+    # logits, dtype, masked, conf, argmax, entropy, mean, G, R, V, ws, ws_bytes, stream
+    assert f(A, 0, None, Bp, None, None, None, 0, 5, 10, None, 0, None) == 0          # nothing to do
+    assert f(A, 3, None, Bp, None, None, None, 1, 5, 10, Wp, 1 << 20, None) == 1      # dtype
+    assert f(A, 0, None, Bp, None, None, None, 1, 5, 0, Wp, 1 << 20, None) == 1       # V
+    assert f(None, 0, None, Bp, None, None, None, 1, 5, 10, Wp, 1 << 20, None) == 1   # logits
+    assert f(A, 0, None, Bp, None, None, None, 1, 5, 10, None, 0, None) == 3          # workspace
+    need = bda.lib.bda_row_stats_workspace_bytes(1, 5, 10)
+    assert need > 0
+    assert f(A, 0, None, Bp, None, None, None, 1, 5, 10, Wp, need - 1, None) == 3
+    assert f(A, 0, None, ctypes.c_void_p((1 << 32) + 16), None, None, None, 1, 5, 10, Wp, need, None) == 1  # overlap

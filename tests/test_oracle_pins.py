@@ -333,3 +333,61 @@ def test_tile_class_reduction():
     assert oracle.tile_class(M, 0, 2, 2, 4) == oracle.EMPTY
     assert oracle.tile_class(M, 0, 4, 0, 4) == oracle.PARTIAL
     assert oracle.tile_class(M, 8, 16, 0, 8) == oracle.EMPTY
+
+
+# ---- row statistics: confidence, argmax, entropy ([DGemma] adaptive stopping)
+
+def test_row_stats_uniform_row():
+    V = 1000
+    conf, am, ent, mean = oracle.row_stats(np.full((1, 3, V), 0.75, np.float32))
+    assert np.allclose(conf, 1.0 / V, rtol=1e-14) and (am == 0).all()
+    assert np.allclose(ent, math.log(V), rtol=1e-13) and np.isclose(mean[0], math.log(V), rtol=1e-13)
+
+
+@pytest.mark.parametrize("V,delta", [(2, 0.5), (1000, 3.0), (131072, 12.0), (50, 40.0)])
+def test_row_stats_single_peak_closed_form(V, delta):
+    row = np.zeros((1, 1, V), np.float32)
+    row[0, 0, V // 3] = delta
+    conf, am, ent, _ = oracle.row_stats(row)
+    den = 1.0 + (V - 1) * math.exp(-delta)
+    p1, q = 1.0 / den, math.exp(-delta) / den
+    H = -p1 * math.log(p1) - (V - 1) * q * math.log(q)
+    assert am[0, 0] == V // 3 and math.isclose(conf[0, 0], p1, rel_tol=1e-12)
+    assert math.isclose(ent[0, 0], H, rel_tol=1e-10, abs_tol=1e-14)
+
+
+def test_row_stats_two_levels_closed_form():
+    V, k, a = 4096, 17, 2.5
+    row = np.zeros((1, 1, V), np.float32)
+    row[0, 0, 100:100 + k] = a
+    _, am, ent, _ = oracle.row_stats(row)
+    den = k * math.exp(a) + (V - k)
+    pa, p0 = math.exp(a) / den, 1.0 / den
+    H = -k * pa * math.log(pa) - (V - k) * p0 * math.log(p0)
+    assert am[0, 0] == 100                         # ties: lowest index
+    assert math.isclose(ent[0, 0], H, rel_tol=1e-12)
+
+
+def test_row_stats_matches_scipy_entropy_and_shift_invariance():
+    import scipy.special
+    import scipy.stats
+    g = np.random.default_rng(11)
+    lg = (np.round(g.standard_normal((3, 5, 700)) * 3 * 256) / 256).astype(np.float32)   # k/256: shifts exact
+    conf, am, ent, mean = oracle.row_stats(lg)
+    p = scipy.special.softmax(lg.astype(np.float64), axis=-1)
+    assert np.allclose(ent, scipy.stats.entropy(p, axis=-1), rtol=1e-11)
+    assert np.allclose(conf, p.max(-1), rtol=1e-12) and (am == lg.argmax(-1)).all()
+    assert np.allclose(mean, ent.mean(-1), rtol=1e-12)
+    c2, a2, e2, _ = oracle.row_stats(lg + np.float32(64.0))   # exact shift in fp32 at these magnitudes
+    assert np.allclose(e2, ent, rtol=1e-11) and (a2 == am).all()
+
+
+def test_row_stats_masked_rows_and_group_mean():
+    g = np.random.default_rng(12)
+    lg = g.standard_normal((2, 6, 64)).astype(np.float32)
+    m = np.array([[1, 0, 1, 0, 0, 1], [0, 0, 0, 0, 0, 0]], np.uint8)
+    conf, am, ent, mean = oracle.row_stats(lg, m)
+    _, _, ent_all, _ = oracle.row_stats(lg)
+    assert np.isnan(ent[m == 0]).all() and (am[m == 0] == -1).all()
+    assert np.allclose(ent[m == 1], ent_all[m == 1], rtol=0, atol=0)
+    assert math.isclose(mean[0], ent_all[0, [0, 2, 5]].mean(), rel_tol=1e-14) and mean[1] == 0.0
