@@ -25,6 +25,7 @@ _ENTRY_POINTS = (
     "bda_attn_fwd", "bda_attn_workspace_bytes", "bda_commit", "bda_commit_workspace_bytes",
     "bda_verify", "bda_verify_workspace_bytes", "bda_classify_tile", "bda_strerror",
     "bda_last_error", "bda_version", "bda_row_stats", "bda_row_stats_workspace_bytes",
+    "bda_attn_fwd_lse",
 )
 
 
@@ -42,6 +43,8 @@ def _load():
     P, I, S, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
     L.bda_attn_fwd.argtypes = [P, P, P, P, I, I, I, I, I, I, I, P, S, P]
     L.bda_attn_fwd.restype = I
+    L.bda_attn_fwd_lse.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P, S, P]
+    L.bda_attn_fwd_lse.restype = I
     L.bda_attn_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     L.bda_attn_workspace_bytes.restype = S
     L.bda_commit.argtypes = [P, I, P, P, F, I, I, I, I, P, S, P]
@@ -104,10 +107,11 @@ def attn_workspace_bytes(B, Hq, Hkv, L, d, block, mode) -> int:
     return int(lib.bda_attn_workspace_bytes(B, Hq, Hkv, L, d, block, MODE[mode] if isinstance(mode, str) else mode))
 
 
-def attn_fwd(q, k, v, mode: str, block: int, out=None, workspace=None):
+def attn_fwd(q, k, v, mode: str, block: int, out=None, workspace=None, lse=None):
     """Masked attention forward (bf16).  HYBRID: q/k/v [B,H,2L,d] over
     [x_t ; x_0]; DECODE/CAUSAL: q [B,Hq,n,d] with n = ``block`` and k/v
-    [B,Hkv,L,d].  Returns ``out`` shaped like q."""
+    [B,Hkv,L,d].  Returns ``out`` shaped like q.  With ``lse`` (float32
+    [B,Hq,rows]) the per-row natural-log log-sum-exp is written too."""
     m = MODE[mode]
     for t in (q, k, v):
         if t.dtype != torch.bfloat16 or t.dim() != 4:
@@ -132,8 +136,15 @@ def attn_fwd(q, k, v, mode: str, block: int, out=None, workspace=None):
     _check_dev(q, out)
     need = attn_workspace_bytes(B, Hq, Hkv, L, d, block, m)
     ws = _workspace(need, dev, workspace)
-    rc = lib.bda_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, L, d, block, m,
-                          _ptr(ws), need, _stream(dev))
+    if lse is None:
+        rc = lib.bda_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, L, d, block, m,
+                              _ptr(ws), need, _stream(dev))
+    else:
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Sq):
+            raise ValueError("lse must be float32 [B, Hq, rows]")
+        _check_dev(q, lse)
+        rc = lib.bda_attn_fwd_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, L, d, block,
+                                  m, _ptr(ws), need, _stream(dev))
     if rc:
         raise BdaError(rc, "bda_attn_fwd")
     return out

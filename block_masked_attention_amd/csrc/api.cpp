@@ -72,8 +72,9 @@ size_t bda_attn_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int block,
   return p.ws_bytes;
 }
 
-int bda_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv,
-                 int L, int d, int block, int mode, void* workspace, size_t ws_bytes, void* stream) {
+static int attn_fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                         int Hq, int Hkv, int L, int d, int block, int mode, void* workspace,
+                         size_t ws_bytes, void* stream) {
   if (int e = check_attn(B, Hq, Hkv, L, d, block, mode)) return e;
   if (!q || !k || !v || !out) return fail(BDA_EINVAL, "q, k, v and out must be non-NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
@@ -84,6 +85,10 @@ int bda_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, 
   const size_t kbytes = (size_t)B * Hkv * Sk * d * 2;
   if (overlap(out, qbytes, q, qbytes) || overlap(out, qbytes, k, kbytes) || overlap(out, qbytes, v, kbytes))
     return fail(BDA_EINVAL, "out overlaps q, k or v");
+  const size_t lbytes = (size_t)B * Hq * Sq * 4;
+  if (lse && (!aligned16(lse) || overlap(lse, lbytes, q, qbytes) || overlap(lse, lbytes, k, kbytes) ||
+              overlap(lse, lbytes, v, kbytes) || overlap(lse, lbytes, out, qbytes)))
+    return fail(BDA_EINVAL, "lse must be 16-byte aligned and must not overlap q, k, v or out");
   bda::AttnPlan p;
   const char* why = "";
   if (int e = bda::attn_make_plan(B, Hq, Hkv, L, d, block, mode, &p, &why))
@@ -94,12 +99,25 @@ int bda_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, 
                   workspace ? ws_bytes : (size_t)0);
     if (!aligned16(workspace)) return fail(BDA_EINVAL, "workspace must be 16-byte aligned");
     if (overlap(workspace, p.ws_bytes, out, qbytes) || overlap(workspace, p.ws_bytes, q, qbytes) ||
-        overlap(workspace, p.ws_bytes, k, kbytes) || overlap(workspace, p.ws_bytes, v, kbytes))
+        overlap(workspace, p.ws_bytes, k, kbytes) || overlap(workspace, p.ws_bytes, v, kbytes) ||
+        (lse && overlap(workspace, p.ws_bytes, lse, lbytes)))
       return fail(BDA_EINVAL, "workspace overlaps a tensor argument");
   }
-  hipError_t e = bda::attn_launch(p, q, k, v, out, workspace, (hipStream_t)stream);
+  hipError_t e = bda::attn_launch(p, q, k, v, out, lse, workspace, (hipStream_t)stream);
   if (e != hipSuccess) return fail(BDA_EHIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+int bda_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv,
+                 int L, int d, int block, int mode, void* workspace, size_t ws_bytes, void* stream) {
+  return attn_fwd_impl(q, k, v, out, nullptr, B, Hq, Hkv, L, d, block, mode, workspace, ws_bytes, stream);
+}
+
+int bda_attn_fwd_lse(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
+                     int Hkv, int L, int d, int block, int mode, void* workspace, size_t ws_bytes,
+                     void* stream) {
+  if (!lse) return fail(BDA_EINVAL, "lse must be non-NULL");
+  return attn_fwd_impl(q, k, v, out, lse, B, Hq, Hkv, L, d, block, mode, workspace, ws_bytes, stream);
 }
 
 static int check_logits(const void* logits, int dtype, int G, int R, int V, const char* gname) {

@@ -34,6 +34,7 @@ struct AttnArgs {
   uint16_t* out;
   float* part_o;    // [split][B*Hq*n][D] unnormalised partial outputs
   float* part_ml;   // [split][B*Hq*n][2] (running max in log2 units, row sum)
+  float* lse;       // optional [B*Hq*Sq]: natural-log log-sum-exp of each row's scores
   int B, Hq, Hkv, G, mode, L, n, blk, Sq, Sk;
   int rows_per_wg, n_qtiles, n_splits, split_keys, pairs_per_xcd;
   int n_items;      // work items (batch x kv head x query tile x key split)
@@ -520,6 +521,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       if (!valid[qb]) continue;
       if (a.n_splits == 1) {
         const float inv = 1.f / l_tot;
+        if (a.lse != nullptr && hb == 0)
+          a.lse[(size_t)(b * a.Hq + head[qb]) * a.Sq + qrow[qb]] = (m_run[qb] * sl2 + __log2f(l_tot)) * 0.6931471805599453f;
         uint16_t* op = a.out + ((size_t)(b * a.Hq + head[qb]) * a.Sq + qrow[qb]) * D + 4 * hb;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
@@ -682,8 +685,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
-                                                           uint16_t* __restrict__ out, long long rows,
-                                                           int n_splits) {
+                                                           uint16_t* __restrict__ out, float* __restrict__ lse,
+                                                           long long rows, int n_splits) {
   constexpr int TPR = D / 4;  // threads per row, 4 elements each
   const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long row = t / TPR;
@@ -702,6 +705,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
     acc += wgt * x;
   }
   const float inv = 1.f / l;
+  if (lse != nullptr && c == 0) lse[row] = (M + __log2f(l)) * 0.6931471805599453f;
   u32x2 pk;
   pk[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
   pk[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
@@ -817,13 +821,14 @@ static hipError_t launch_d(const AttnPlan& p, AttnArgs a, hipStream_t st) {
   const long long threads = rows * (D / 4);
   const long long blocks = (threads + 255) / 256;
   hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, st, a.part_o,
-                     a.part_ml, a.out, rows, p.n_splits);
+                     a.part_ml, a.out, a.lse, rows, p.n_splits);
   return hipGetLastError();
 }
 
 hipError_t attn_launch(const AttnPlan& p, const void* q, const void* k, const void* v, void* out,
-                       void* ws, hipStream_t st) {
+                       float* lse, void* ws, hipStream_t st) {
   AttnArgs a{};
+  a.lse = lse;
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k;
   a.v = (const uint16_t*)v;

@@ -27,7 +27,7 @@ struct AttnPlan {
 int attn_make_plan(int B, int Hq, int Hkv, int L, int d, int block, int mode, AttnPlan* p,
                    const char** why);
 hipError_t attn_launch(const AttnPlan& p, const void* q, const void* k, const void* v, void* out,
-                       void* ws, hipStream_t st);
+                       float* lse, void* ws, hipStream_t st);
 
 struct CommitPlan {
   int G, R, V, dtype;

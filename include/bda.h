@@ -85,6 +85,17 @@ int bda_attn_fwd(const void* q, const void* k, const void* v, void* out,
 size_t bda_attn_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int block, int mode);
 
 /*
+ * The same forward, also writing lse [B, Hq, Sq] (fp32, device, caller-owned,
+ * 16-byte aligned): the natural-log log-sum-exp of each query row's scaled
+ * allowed scores, log sum_j exp(scale * q.k_j).  It is what the backward
+ * (bda_attn_bwd) takes to rebuild the softmax.  Same workspace as
+ * bda_attn_fwd.  lse must not overlap any other argument.
+ */
+int bda_attn_fwd_lse(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int B, int Hq, int Hkv, int L, int d, int block, int mode,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * Confidence commit ([LLaDA] SPRINT; [DGemma] Schedulers; [VLM-8B]).
  * logits: [G, R, V] of dtype BDA_BF16 or BDA_F32 (G independent groups, e.g.
  *   sequences; R canvas positions; V vocabulary).  Values must be finite.

@@ -54,9 +54,10 @@ def _load():
     lib.oracle_commit.argtypes = [P, P, P, F, L, L, L, L, P, P, P, P, I]
     lib.oracle_verify.argtypes = [P, P, P, P, L, L, L, I]
     lib.oracle_row_stats.argtypes = [P, P, P, P, P, P, L, L, L, I]
+    lib.oracle_attention_bwd.argtypes = [I, P, P, P, P, P, P, P, P, L, L, L, L, L, L, I]
     lib.oracle_max_threads.restype = I
     for f in (lib.oracle_mask_shape, lib.oracle_mask, lib.oracle_attention,
-              lib.oracle_commit, lib.oracle_verify, lib.oracle_row_stats):
+              lib.oracle_commit, lib.oracle_verify, lib.oracle_row_stats, lib.oracle_attention_bwd):
         f.restype = I
     _lib = lib
     return lib
@@ -108,6 +109,24 @@ def attention(mode: str, q, k, v, L: int, block: int, sel=None, nthreads: int = 
     if rc:
         raise ValueError("oracle_attention: bad arguments")
     return out
+
+
+def attention_bwd(mode: str, q, k, v, dout, L: int, block: int, nthreads: int = 0):
+    """Gradients of sum(dout * attention(q, k, v)) in double: (dq, dk, dv,
+    lse) with lse the natural-log log-sum-exp of each query row's scores."""
+    lib = _load()
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    B, Hq, rows, d = q.shape
+    Hkv = k.shape[1]
+    dq = np.empty(q.shape, dtype=np.float64)
+    dk = np.empty(k.shape, dtype=np.float64)
+    dv = np.empty(v.shape, dtype=np.float64)
+    lse = np.empty((B, Hq, rows), dtype=np.float64)
+    rc = lib.oracle_attention_bwd(MODES[mode], _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk),
+                                  _ptr(dv), _ptr(lse), B, Hq, Hkv, L, d, block, nthreads)
+    if rc:
+        raise ValueError("oracle_attention_bwd: bad arguments")
+    return dq, dk, dv, lse
 
 
 def commit(logits, masked, tokens, threshold: float, k_min: int, nthreads: int = 0):

@@ -201,6 +201,105 @@ int oracle_attention(int mode, const float* q, const float* k, const float* v, d
     return fail;
 }
 
+/*
+ * Gradients of the masked attention above (the training form's backward;
+ * the BDLM objective of [LLaDA] trains through this attention).  With
+ * loss = sum(dout * out), for every (b, h) and query row i with allowed set
+ * A_i, s_ij = scale q_i.k_j, p_ij = softmax_j(s_i), o_i = sum_j p_ij v_j:
+ *   dv_j   += p_ij dout_i                            (summed over rows, heads)
+ *   dP_ij   = dout_i . v_j
+ *   dS_ij   = p_ij (dP_ij - dout_i . o_i)
+ *   dq_i    = scale sum_j dS_ij k_j
+ *   dk_j   += scale dS_ij q_i                        (summed over rows, heads)
+ * and lse_i = log sum_{j in A_i} exp(s_ij).  dq: [B,Hq,rows,d]; dk, dv:
+ * [B,Hkv,keys,d]; lse: [B,Hq,rows] (may be NULL).  The G = Hq/Hkv query
+ * heads of a kv head accumulate into its dk, dv; each (b, kv head) is one
+ * task, so the sums run in a fixed order.
+ */
+int oracle_attention_bwd(int mode, const float* q, const float* k, const float* v, const float* dout,
+                         double* dq, double* dk, double* dv, double* lse, long B, long Hq, long Hkv,
+                         long L, long d, long block, int nthreads)
+{
+    long rows, keys;
+    if (oracle_mask_shape(mode, L, block, &rows, &keys)) return 1;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv) return 1;
+    uint8_t* M = (uint8_t*)malloc((size_t)rows * (size_t)keys);
+    if (!M) return 1;
+    oracle_mask(mode, L, block, M);
+    const double scale = 1.0 / sqrt((double)d);
+    const long group = Hq / Hkv;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int fail = 0;
+#pragma omp parallel
+    {
+        double* p = (double*)malloc(sizeof(double) * (size_t)keys);
+        double* o = (double*)malloc(sizeof(double) * (size_t)d);
+        if (!p || !o) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (long t = 0; t < B * Hkv; ++t) {
+                const long b = t / Hkv, g = t % Hkv;
+                const float* K = k + (b * Hkv + g) * keys * d;
+                const float* Vv = v + (b * Hkv + g) * keys * d;
+                double* dK = dk + (b * Hkv + g) * keys * d;
+                double* dV = dv + (b * Hkv + g) * keys * d;
+                for (long x = 0; x < keys * d; ++x) { dK[x] = 0.0; dV[x] = 0.0; }
+                for (long h = g * group; h < (g + 1) * group; ++h) {
+                    for (long i = 0; i < rows; ++i) {
+                        const float* qi = q + ((b * Hq + h) * rows + i) * d;
+                        const float* gi = dout + ((b * Hq + h) * rows + i) * d;
+                        double* dqi = dq + ((b * Hq + h) * rows + i) * d;
+                        const uint8_t* Mi = M + i * keys;
+                        double m = -INFINITY;
+                        for (long j = 0; j < keys; ++j) {
+                            p[j] = 0.0;
+                            if (!Mi[j]) continue;
+                            double acc = 0.0;
+                            for (long c = 0; c < d; ++c) acc += (double)qi[c] * (double)K[j * d + c];
+                            p[j] = acc * scale;
+                            if (p[j] > m) m = p[j];
+                        }
+                        double Z = 0.0;
+                        for (long j = 0; j < keys; ++j)
+                            if (Mi[j]) { p[j] = exp(p[j] - m); Z += p[j]; }
+                        for (long c = 0; c < d; ++c) o[c] = 0.0;
+                        for (long j = 0; j < keys; ++j) {
+                            if (!Mi[j]) continue;
+                            p[j] /= Z;
+                            for (long c = 0; c < d; ++c) o[c] += p[j] * (double)Vv[j * d + c];
+                        }
+                        if (lse) lse[(b * Hq + h) * rows + i] = m + log(Z);
+                        double Di = 0.0;
+                        for (long c = 0; c < d; ++c) Di += (double)gi[c] * o[c];
+                        for (long c = 0; c < d; ++c) dqi[c] = 0.0;
+                        for (long j = 0; j < keys; ++j) {
+                            if (!Mi[j]) continue;
+                            double dP = 0.0;
+                            for (long c = 0; c < d; ++c) dP += (double)gi[c] * (double)Vv[j * d + c];
+                            const double dS = p[j] * (dP - Di);
+                            for (long c = 0; c < d; ++c) {
+                                dqi[c] += scale * dS * (double)K[j * d + c];
+                                dK[j * d + c] += scale * dS * (double)qi[c];
+                                dV[j * d + c] += p[j] * (double)gi[c];
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        free(p);
+        free(o);
+    }
+    free(M);
+    return fail;
+}
+
 /* ---------------------------------------------------------------------- */
 /* Confidence commit ([LLaDA] SPRINT; [DGemma] Schedulers)                  */
 /* ---------------------------------------------------------------------- */

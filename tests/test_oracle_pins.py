@@ -391,3 +391,76 @@ def test_row_stats_masked_rows_and_group_mean():
     assert np.isnan(ent[m == 0]).all() and (am[m == 0] == -1).all()
     assert np.allclose(ent[m == 1], ent_all[m == 1], rtol=0, atol=0)
     assert math.isclose(mean[0], ent_all[0, [0, 2, 5]].mean(), rel_tol=1e-14) and mean[1] == 0.0
+
+
+# ---- backward of the masked attention (training form)
+
+def _torch_attention64(mode, q, k, v, L, block):
+    """Masked softmax attention in torch float64 on the oracle's dense mask
+    (the mask itself is pinned above); GQA by repeating kv heads."""
+    M = torch.from_numpy(oracle.mask(mode, L, block).astype(bool))
+    G = q.shape[1] // k.shape[1]
+    kk = k.repeat_interleave(G, dim=1)
+    vv = v.repeat_interleave(G, dim=1)
+    s = (q @ kk.transpose(-1, -2)) / math.sqrt(q.shape[-1])
+    s = s.masked_fill(~M, float("-inf"))
+    return torch.softmax(s, dim=-1) @ vv, torch.logsumexp(s, dim=-1)
+
+
+BWD_CASES = [("hybrid", 1, 4, 2, 12, 3, 8), ("hybrid", 2, 2, 1, 10, 4, 16), ("hybrid", 1, 2, 2, 7, 7, 4),
+             ("decode", 1, 4, 2, 15, 5, 8), ("causal", 2, 2, 1, 13, 6, 8), ("causal", 1, 2, 2, 9, 9, 4)]
+
+
+def _bwd_inputs(mode, B, Hq, Hkv, L, blk, d, seed):
+    g = torch.Generator().manual_seed(seed)
+    rows = 2 * L if mode == "hybrid" else blk
+    keys = 2 * L if mode == "hybrid" else L
+    mk = lambda *s: torch.randn(*s, generator=g).to(torch.float32)
+    return mk(B, Hq, rows, d), mk(B, Hkv, keys, d), mk(B, Hkv, keys, d), mk(B, Hq, rows, d)
+
+
+@pytest.mark.parametrize("mode,B,Hq,Hkv,L,blk,d", BWD_CASES)
+def test_attention_bwd_matches_autograd(mode, B, Hq, Hkv, L, blk, d):
+    q, k, v, do = _bwd_inputs(mode, B, Hq, Hkv, L, blk, d, seed=L * 7 + d)
+    dq, dk, dv, lse = oracle.attention_bwd(mode, q, k, v, do, L, blk)
+    q6, k6, v6 = (t.double().requires_grad_(True) for t in (q, k, v))
+    out, lse_t = _torch_attention64(mode, q6, k6, v6, L, blk)
+    (out * do.double()).sum().backward()
+    assert np.allclose(dq, q6.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(dk, k6.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(dv, v6.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(lse, lse_t.detach().numpy(), rtol=1e-12)
+
+
+def test_attention_bwd_finite_differences():
+    mode, B, Hq, Hkv, L, blk, d = "hybrid", 1, 2, 1, 6, 2, 4
+    q, k, v, do = _bwd_inputs(mode, B, Hq, Hkv, L, blk, d, seed=5)
+    dq, dk, dv, _ = oracle.attention_bwd(mode, q, k, v, do, L, blk)
+    base = {"q": q.double(), "k": k.double(), "v": v.double()}
+
+    def loss(**kw):
+        t = dict(base, **kw)
+        out, _ = _torch_attention64(mode, t["q"], t["k"], t["v"], L, blk)
+        return float((out * do.double()).sum())
+
+    g = np.random.default_rng(3)
+    eps = 1e-6
+    for name, grad in (("q", dq), ("k", dk), ("v", dv)):
+        for _ in range(6):
+            idx = tuple(int(g.integers(s)) for s in base[name].shape)
+            plus, minus = base[name].clone(), base[name].clone()
+            plus[idx] += eps
+            minus[idx] -= eps
+            fd = (loss(**{name: plus}) - loss(**{name: minus})) / (2 * eps)
+            assert math.isclose(grad[idx], fd, rel_tol=1e-6, abs_tol=1e-8), (name, idx, grad[idx], fd)
+
+
+def test_attention_bwd_zero_upstream_rows_send_nothing_to_their_private_keys():
+    # x_t keys of block j are seen only by the x_t rows of block j: zero dout
+    # there and those keys get no gradient at all.
+    mode, L, blk = "hybrid", 8, 2
+    q, k, v, do = _bwd_inputs(mode, 1, 2, 1, L, blk, 8, seed=9)
+    do[:, :, 2:4] = 0.0                       # x_t rows of block 1
+    _, dk, dv, _ = oracle.attention_bwd(mode, q, k, v, do, L, blk)
+    assert np.abs(dk[:, :, 2:4]).max() == 0.0 and np.abs(dv[:, :, 2:4]).max() == 0.0
+    assert np.abs(dk[:, :, 4:6]).max() > 0.0
