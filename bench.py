@@ -254,6 +254,25 @@ def secondary(bda, synth, torch, dev, args):
         del sets, out, ws
         torch.cuda.empty_cache()
 
+    # ---- training-form backward (dq, dk, dv) on the headline workload:
+    # 2.5x the forward's unmasked FLOPs (dS, dP, dQ, dK, dV: five products)
+    case = synth.hybrid_train()
+    B, Hq, S, d = case.q.shape
+    q, k, v = case.q.to(dev), case.k.to(dev), case.v.to(dev)
+    do = torch.randn(q.shape, generator=torch.Generator(device=dev).manual_seed(3), device=dev).to(torch.bfloat16)
+    lse = torch.empty(B, Hq, S, dtype=torch.float32, device=dev)
+    out = bda.attn_fwd(q, k, v, "hybrid", case.block, lse=lse)
+    bws = torch.empty(bda.lib.bda_attn_bwd_workspace_bytes(B, Hq, k.shape[1], case.L, d, case.block, 0),
+                      dtype=torch.uint8, device=dev)
+    mean, med = time_launches(lambda i: bda.attn_bwd(q, k, v, out, do, lse, case.block, workspace=bws), iters, 5)
+    fl = 2.5 * 4 * d * hybrid_pairs(case.L, case.block) * B * Hq
+    res["training_backward"] = {"B": B, "L": case.L, "block": case.block, "us_per_call": round(mean * 1e3, 2),
+                                "TFLOP/s": round(fl / (mean * 1e-3) / 1e12, 2),
+                                "mfma_frac": round(fl / (mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    log(f"[bench] training_backward: {res['training_backward']}")
+    del q, k, v, do, lse, out, bws
+    torch.cuda.empty_cache()
+
     # ---- multimodal prefill: causal over the 4096-token prefix, B=2
     case = synth.multimodal_prefill()
     B, Hq, n, d = case.q.shape

@@ -25,7 +25,7 @@ _ENTRY_POINTS = (
     "bda_attn_fwd", "bda_attn_workspace_bytes", "bda_commit", "bda_commit_workspace_bytes",
     "bda_verify", "bda_verify_workspace_bytes", "bda_classify_tile", "bda_strerror",
     "bda_last_error", "bda_version", "bda_row_stats", "bda_row_stats_workspace_bytes",
-    "bda_attn_fwd_lse",
+    "bda_attn_fwd_lse", "bda_attn_bwd", "bda_attn_bwd_workspace_bytes",
 )
 
 
@@ -45,6 +45,10 @@ def _load():
     L.bda_attn_fwd.restype = I
     L.bda_attn_fwd_lse.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P, S, P]
     L.bda_attn_fwd_lse.restype = I
+    L.bda_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, S, P]
+    L.bda_attn_bwd.restype = I
+    L.bda_attn_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    L.bda_attn_bwd_workspace_bytes.restype = S
     L.bda_attn_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     L.bda_attn_workspace_bytes.restype = S
     L.bda_commit.argtypes = [P, I, P, P, F, I, I, I, I, P, S, P]
@@ -148,6 +152,32 @@ def attn_fwd(q, k, v, mode: str, block: int, out=None, workspace=None, lse=None)
     if rc:
         raise BdaError(rc, "bda_attn_fwd")
     return out
+
+
+def attn_bwd(q, k, v, out, dout, lse, block: int, workspace=None):
+    """Backward of the training form (hybrid mask): returns (dq, dk, dv) for
+    loss = sum(dout * out); ``lse`` from attn_fwd(..., lse=...)."""
+    for t in (q, k, v, out, dout):
+        if t.dtype != torch.bfloat16 or t.dim() != 4:
+            raise ValueError("q, k, v, out, dout must be 4-D bfloat16")
+    dev = _check_dev(q, k, v, out, dout, lse)
+    B, Hq, Sq, d = q.shape
+    Hkv = k.shape[1]
+    if Sq % 2 or k.shape != v.shape or k.shape[2] != Sq or out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("shape mismatch")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Sq):
+        raise ValueError("lse must be float32 [B, Hq, 2L]")
+    L = Sq // 2
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    need = int(lib.bda_attn_bwd_workspace_bytes(B, Hq, Hkv, L, d, block, 0))
+    ws = _workspace(need, dev, workspace)
+    rc = lib.bda_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                          _ptr(dv), B, Hq, Hkv, L, d, block, 0, _ptr(ws), need, _stream(dev))
+    if rc:
+        raise BdaError(rc, "bda_attn_bwd")
+    return dq, dk, dv
 
 
 def commit(logits, tokens, masked, threshold: float, k_min: int, workspace=None):

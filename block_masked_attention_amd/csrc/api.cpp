@@ -190,6 +190,53 @@ int bda_verify(const void* logits, int dtype, const int64_t* drafts, int64_t* ar
   return ok();
 }
 
+size_t bda_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int block, int mode) {
+  if (mode != BDA_MODE_HYBRID || check_attn(B, Hq, Hkv, L, d, block, mode) != BDA_OK) return 0;
+  bda::BwdPlan p;
+  const char* why = "";
+  if (bda::bwd_make_plan(B, Hq, Hkv, L, d, block, &p, &why)) return 0;
+  return p.ws_bytes;
+}
+
+int bda_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int L, int d,
+                 int block, int mode, void* workspace, size_t ws_bytes, void* stream) {
+  if (int e = check_attn(B, Hq, Hkv, L, d, block, mode)) return e;
+  if (mode != BDA_MODE_HYBRID) return fail(BDA_EUNSUPPORTED, "the backward is implemented for the hybrid form only");
+  const void* in[] = {q, k, v, out, dout, lse, dq, dk, dv};
+  for (const void* x : in)
+    if (!x) return fail(BDA_EINVAL, "q, k, v, out, dout, lse, dq, dk and dv must be non-NULL");
+  for (const void* x : in)
+    if (!aligned16(x)) return fail(BDA_EINVAL, "all tensors must be 16-byte aligned");
+  const size_t S = 2 * (size_t)L;
+  const size_t qb = (size_t)B * Hq * S * d * 2, kb = (size_t)B * Hkv * S * d * 2, lb = (size_t)B * Hq * S * 4;
+  const void* ins[] = {q, k, v, out, dout, lse};
+  const size_t insz[] = {qb, kb, kb, qb, qb, lb};
+  void* outs[] = {dq, dk, dv};
+  const size_t outsz[] = {qb, kb, kb};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlap(outs[i], outsz[i], ins[j], insz[j])) return fail(BDA_EINVAL, "gradients must not overlap inputs");
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return fail(BDA_EINVAL, "gradients must not overlap");
+  }
+  bda::BwdPlan p;
+  const char* why = "";
+  if (int e = bda::bwd_make_plan(B, Hq, Hkv, L, d, block, &p, &why))
+    return fail(e == 2 ? BDA_EUNSUPPORTED : BDA_EINVAL, "%s", why);
+  if (!workspace || ws_bytes < p.ws_bytes)
+    return fail(BDA_EWORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_bytes,
+                workspace ? ws_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(BDA_EINVAL, "workspace must be 16-byte aligned");
+  for (int j = 0; j < 6; ++j)
+    if (overlap(workspace, p.ws_bytes, ins[j], insz[j])) return fail(BDA_EINVAL, "workspace overlaps an input");
+  for (int i = 0; i < 3; ++i)
+    if (overlap(workspace, p.ws_bytes, outs[i], outsz[i])) return fail(BDA_EINVAL, "workspace overlaps a gradient");
+  hipError_t e = bda::bwd_launch(p, q, k, v, out, dout, lse, dq, dk, dv, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BDA_EHIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 size_t bda_row_stats_workspace_bytes(int G, int R, int V) { return bda_commit_workspace_bytes(G, R, V); }
 
 int bda_row_stats(const void* logits, int dtype, const uint8_t* masked, float* conf, int64_t* argmax_out,

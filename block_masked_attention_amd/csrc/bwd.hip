@@ -1,0 +1,634 @@
+// Backward of the hybrid-mask attention (the training form) for gfx950.
+//
+// The forward is the block-diffusion attention over [x_t ; x_0] ("Block
+// Diffusion Attention", sec. 1 of the Nemotron-Labs-Diffusion-8B-Base 3x
+// analysis page; the BDLM objective of the LLaDA2.0-Uni summary trains
+// through it).  With P = softmax(scale Q K^T) over the allowed keys and the
+// per-row log-sum-exp from the forward, for loss = sum(dO * O):
+//   dV = P^T dO,   dP = dO V^T,   dS = P (dP - D),  D_i = sum_c dO_ic O_ic,
+//   dQ = scale dS K,   dK = scale dS^T Q.
+// Three launches:
+//   delta  D per query row (one pass over O and dO).
+//   dq     query-stationary, like the forward: per key tile S^T = K Q^T,
+//          dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T (K^T by the LDS
+//          transpose read, dS^T straight from the accumulator registers).
+//   dkdv   key-stationary: a workgroup keeps 128 keys (32 per wavefront) of
+//          one (batch, kv head) in LDS and streams the blocks of 32 query
+//          slots (rows x heads of the group) that see them:
+//          S = Q K^T, dP = dO V^T (lane = key), dV += P^T dO and
+//          dK += dS^T Q (dO and Q by the LDS transpose read).
+// P is rebuilt exactly from the log-sum-exp (no running max); masked pairs
+// get P = 0.  fp32 accumulation, bf16 MFMA operands, bf16 gradients.
+#include "common.h"
+#include "geometry.h"
+#include "internal.h"
+#include "tiles.h"
+
+namespace bda {
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;     // [B*Hq*S] natural log
+  float* delta;         // [B*Hq*S] workspace
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  int B, Hq, Hkv, G, L, blk, S;
+  int rows_per_wg, n_qtiles;   // dq: query tile size (per half) and count
+  int nkh;                     // dkdv: 128-key tiles per half
+  int pairs_per_xcd;
+  float sl2, scale;
+};
+
+constexpr float kLn2Inv = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// D_i = sum_c dO_ic O_ic (fp32), one row per D/8 lanes.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restrict__ o,
+                                                        const uint16_t* __restrict__ dout,
+                                                        float* __restrict__ delta, long long rows) {
+  constexpr int TPR = D / 8;
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = t / TPR;
+  const int c = (int)(t - row * TPR);
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 x = *(const u32x4*)(o + row * D + 8 * c);
+    const u32x4 y = *(const u32x4*)(dout + row * D + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc += bf16_lo(x[e]) * bf16_lo(y[e]) + bf16_hi(x[e]) * bf16_hi(y[e]);
+  }
+#pragma unroll
+  for (int off = TPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && c == 0) delta[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// dQ.  One workgroup per (batch, kv head, query tile) as in the forward's
+// training form: NW wavefronts x 32 query slots, half of them on x_t rows
+// and half on the same positions of x_0.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdArgs a) {
+  constexpr int KSTEPS = D / 16, DT = D / 32, CPR = D / 8;
+  constexpr int BN = 64, TCH = BN * CPR, NT = NW * 64, CU = (TCH + NT - 1) / NT, TE = BN * D;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TE];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, ql = lane & 31, hb = lane >> 5;
+  const int P = a.B * a.Hkv;
+  int pair, qt;
+  {
+    const int bid = blockIdx.x;
+    if (a.pairs_per_xcd > 0) {
+      const int xcd = bid & 7, i = bid >> 3;
+      pair = xcd * a.pairs_per_xcd + i % a.pairs_per_xcd;
+      qt = a.n_qtiles - 1 - i / a.pairs_per_xcd;
+    } else {
+      pair = bid % P;
+      qt = a.n_qtiles - 1 - bid / P;
+    }
+  }
+  const int b = pair / a.Hkv, g = pair - b * a.Hkv;
+  const int per_half = NW / 2, half = w / per_half;
+  const int s = (w - half * per_half) * 32 + ql;
+  const int rloc = s / a.G;
+  const int pos = qt * a.rows_per_wg + rloc;
+  const bool valid = rloc < a.rows_per_wg && pos < a.L;
+  const int qrow = half * a.L + pos;
+  const int head = g * a.G + (s - rloc * a.G);
+  const size_t rowi = (size_t)(b * a.Hq + head) * a.S + qrow;
+
+  // key ranges of the tile (as in the forward)
+  const int p0 = qt * a.rows_per_wg;
+  const int p1 = imin(a.L, p0 + a.rows_per_wg);
+  const int e = imin(a.L, ((p1 - 1) / a.blk + 1) * a.blk);
+  const int s_min = (p0 / a.blk) * a.blk;
+  const Span F{a.L, a.L + (s_min / BN) * BN};
+  const Span R1{F.hi, a.L + e};
+  const Span R2{s_min, e};
+  const int nf = (F.hi - F.lo) / BN;
+  const int n1 = R1.hi > R1.lo ? (R1.hi - R1.lo + BN - 1) / BN : 0;
+  const int n2 = R2.hi > R2.lo ? (R2.hi - R2.lo + BN - 1) / BN : 0;
+  const int nt = nf + n1 + n2;
+  auto tile = [&](int j, int& t0, int& t1) {
+    j = imin(j, nt - 1);
+    if (j < nf) {
+      t0 = F.lo + j * BN;
+      t1 = t0 + BN;
+    } else if (j < nf + n1) {
+      t0 = R1.lo + (j - nf) * BN;
+      t1 = imin(R1.hi, t0 + BN);
+    } else {
+      t0 = R2.lo + (j - nf - n1) * BN;
+      t1 = imin(R2.hi, t0 + BN);
+    }
+  };
+
+  bf16x8 qreg[KSTEPS], dreg[KSTEPS];
+  {
+    const uint16_t* qp = a.q + rowi * D + 8 * hb;
+    const uint16_t* dp = a.dout + rowi * D + 8 * hb;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const u32x4 x = valid ? *(const u32x4*)(qp + 16 * ks) : u32x4{0, 0, 0, 0};
+      const u32x4 y = valid ? *(const u32x4*)(dp + 16 * ks) : u32x4{0, 0, 0, 0};
+      qreg[ks] = __builtin_bit_cast(bf16x8, x);
+      dreg[ks] = __builtin_bit_cast(bf16x8, y);
+    }
+  }
+  const float lse2 = valid ? a.lse[rowi] * kLn2Inv : INFINITY;
+  const float dl = valid ? a.delta[rowi] : 0.f;
+  Span A{0, 0}, C{0, 0};
+  if (valid) row_spans(kHybrid, a.L, 2 * a.L, a.blk, qrow, A, C);
+
+  const size_t kvoff = (size_t)pair * a.S * D;
+  const uint16_t* kbase = a.k + kvoff;
+  const uint16_t* vbase = a.v + kvoff;
+
+  const int k_row = ql * D;
+  const int k_swz = swz<D>(ql) & (CPR - 1);
+  int t_lo[DT], t_hi[DT];   // transpose-read offsets: rows 4*hb + j/4 and 8 further
+  {
+    const int j = lane & 15, gi = lane >> 4;
+    const int r = 4 * hb + (j >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int dcol = 32 * dt + 16 * (gi & 1) + 4 * (j & 3);
+      t_lo[dt] = chunk_off<D>(r, dcol >> 3) + (dcol & 7);
+      t_hi[dt] = chunk_off<D>(r + 8, dcol >> 3) + (dcol & 7);
+    }
+  }
+
+  u32x4 kreg[CU], vreg[CU];
+  auto fetch = [&](int j) {
+    int t0, t1;
+    tile(j, t0, t1);
+#pragma unroll
+    for (int u = 0; u < CU; ++u) {
+      const int ch = tid + u * NT;
+      if (TCH % NT == 0 || ch < TCH) {
+        const int r = ch / CPR, c = ch % CPR;
+        const size_t off = (size_t)imin(t0 + r, t1 - 1) * D + 8 * c;
+        kreg[u] = *(const u32x4*)(kbase + off);
+        vreg[u] = *(const u32x4*)(vbase + off);
+      }
+    }
+  };
+  auto lstore = [&](uint16_t* st) {
+#pragma unroll
+    for (int u = 0; u < CU; ++u) {
+      const int ch = tid + u * NT;
+      if (TCH % NT == 0 || ch < TCH) {
+        const int off = chunk_off<D>(ch / CPR, ch % CPR);
+        *(u32x4*)(st + off) = kreg[u];
+        *(u32x4*)(st + TE + off) = vreg[u];
+      }
+    }
+  };
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+
+  auto subtile = [&](const uint16_t* st, int j, int sub) {
+    int t0, t1;
+    tile(j, t0, t1);
+    const int e0 = t0 + 32 * sub, e1 = imin(t1, e0 + 32);
+    if (e0 >= e1) return;
+    const int c = inside(A, e0, e1) + inside(C, e0, e1);
+    const bool full = __all(!valid || (e1 - e0 == 32 && c == 32));
+    if (__all(!valid || c == 0)) return;
+    const uint16_t* kr = st + 32 * sub * D + k_row;
+    const uint16_t* vr = st + TE + 32 * sub * D + k_row;
+    f32x16 sv{}, dp{};
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const int co = 8 * ((2 * ks + hb) ^ k_swz);
+      sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(kr + co), qreg[ks], sv, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vr + co), dreg[ks], dp, 0, 0, 0);
+    }
+    bf16x8 dsb[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      u32x4 pk;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        float d2[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int i = 8 * kk + 2 * e2 + h;
+          const int jj = e0 + 8 * (i >> 2) + 4 * hb + (i & 3);
+          const bool ok = full || (jj < e1 && (in_span(A, jj) || in_span(C, jj)));
+          const float p = ok ? exp2_fast(fmaf(sv[i], a.sl2, -lse2)) : 0.f;
+          d2[h] = p * (dp[i] - dl);
+        }
+        pk[e2] = pack_bf16x2(d2[0], d2[1]);
+      }
+      dsb[kk] = __builtin_bit_cast(bf16x8, pk);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const uint16_t* kt = st + 16 * (2 * sub + kk) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const s16x4 lo = lds_read_tr(kt + t_lo[dt]);
+        const s16x4 hi = lds_read_tr(kt + t_hi[dt]);
+        const bf16x8 kop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, dsb[kk], acc[dt], 0, 0, 0);
+      }
+    }
+  };
+
+  if (nt > 0) {
+    fetch(0);
+    lstore(smem);
+    fetch(1);
+    __syncthreads();
+    int st = 0;
+#pragma unroll 1
+    for (int j = 0; j < nt; ++j) {
+      const uint16_t* cur = smem + st * 2 * TE;
+      subtile(cur, j, 0);
+      subtile(cur, j, 1);
+      lstore(smem + (st ^ 1) * 2 * TE);
+      fetch(j + 2);
+      __syncthreads();
+      st ^= 1;
+    }
+  }
+
+  // dq = scale * dQ^T; lane (ql, hb) holds d = 32*dt + 8*(i/4) + 4*hb + (i%4)
+  if (valid) {
+    uint16_t* op = a.dq + rowi * D + 4 * hb;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        u32x2 pk;
+        pk[0] = pack_bf16x2(acc[dt][4 * i4] * a.scale, acc[dt][4 * i4 + 1] * a.scale);
+        pk[1] = pack_bf16x2(acc[dt][4 * i4 + 2] * a.scale, acc[dt][4 * i4 + 3] * a.scale);
+        *(u32x2*)(op + 32 * dt + 8 * i4) = pk;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV.  One workgroup of 4 wavefronts per (batch, kv head, 128-key tile of
+// one half); wavefront w owns keys 32w .. 32w+31 of the tile.  The query
+// slots that see the tile are streamed in blocks of 32 (rows x the G heads
+// of the kv head), staged in LDS through registers, double-buffered.
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
+  constexpr int KSTEPS = D / 16, DT = D / 32, CPR = D / 8;
+  constexpr int TK = 128, NT = 256;
+  constexpr int KE = TK * D;                   // elements of the K (or V) tile
+  constexpr int QE = 32 * D;                   // elements of a Q (or dO) block
+  constexpr int QCH = 32 * CPR;                // chunks of a Q block
+  constexpr int QU = (QCH + NT - 1) / NT;      // chunks per thread per matrix
+  __shared__ __attribute__((aligned(16))) uint16_t kv[2 * KE];
+  __shared__ __attribute__((aligned(16))) uint16_t qd[2][2 * QE];
+  __shared__ __attribute__((aligned(16))) float sl[2][2][32];   // lse2, delta per slot
+  __shared__ int srow[2][32];                                   // query row of each slot, -1 if none
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, ql = lane & 31, hb = lane >> 5;
+  const int nk = 2 * a.nkh;
+  int pair, j;
+  {
+    const int bid = blockIdx.x;
+    if (a.pairs_per_xcd > 0) {
+      const int xcd = bid & 7, i = bid >> 3;
+      pair = xcd * a.pairs_per_xcd + i % a.pairs_per_xcd;
+      j = i / a.pairs_per_xcd;
+    } else {
+      const int P = a.B * a.Hkv;
+      pair = bid % P;
+      j = bid / P;
+    }
+  }
+  (void)nk;
+  // heaviest first: clean (x_0) tiles from the start of the sequence, then
+  // the noisy (x_t) tiles, which only their own blocks' rows see
+  const bool clean = j < a.nkh;
+  const int kp0 = (clean ? j : j - a.nkh) * TK;          // first key position of the tile
+  const int kp1 = imin(a.L, kp0 + TK);
+  const int kbase_row = (clean ? a.L : 0) + kp0;        // key-tensor row of the tile's first key
+  const int b = pair / a.Hkv, g = pair - b * a.Hkv;
+  const size_t kvoff = (size_t)pair * a.S * D;
+
+  // the tile's K and V into LDS (rows past the half's end repeat its last key)
+#pragma unroll
+  for (int u = 0; u < (TK * CPR) / NT; ++u) {
+    const int ch = tid + u * NT;
+    const int r = ch / CPR, c = ch % CPR;
+    const size_t off = kvoff + (size_t)(kbase_row + imin(r, kp1 - kp0 - 1)) * D + 8 * c;
+    const int lo = chunk_off<D>(r, c);
+    *(u32x4*)(kv + lo) = *(const u32x4*)(a.k + off);
+    *(u32x4*)(kv + KE + lo) = *(const u32x4*)(a.v + off);
+  }
+
+  // query rows that see the tile: up to two position ranges
+  const int jb = kp0 / a.blk;
+  int ra0, ra1, rb0, rb1;                       // positions [ra0, ra1) of half ha, [rb0, rb1) of x_t
+  int ha;
+  if (clean) {
+    ha = 1;                                     // x_0 rows of blocks >= jb
+    ra0 = jb * a.blk;
+    ra1 = a.L;
+    rb0 = imin(a.L, (jb + 1) * a.blk);          // x_t rows of blocks > jb
+    rb1 = a.L;
+  } else {
+    ha = 0;                                     // x_t rows of the tile's own blocks
+    ra0 = jb * a.blk;
+    ra1 = imin(a.L, ((kp1 - 1) / a.blk + 1) * a.blk);
+    rb0 = rb1 = 0;
+  }
+  const int rpb = 32 / a.G;                     // rows per block of 32 slots
+  const int na = ra1 > ra0 ? (ra1 - ra0 + rpb - 1) / rpb : 0;
+  const int nb = rb1 > rb0 ? (rb1 - rb0 + rpb - 1) / rpb : 0;
+  const int nblk = na + nb;
+
+  // staging of block t: Q and dO chunks through registers
+  u32x4 qreg[QU], dreg[QU];
+  float slv[2];
+  int srv = -1;
+  auto block_row0 = [&](int t, int& half, int& r0, int& r1) {
+    if (t < na) {
+      half = ha;
+      r0 = ra0 + t * rpb;
+      r1 = ra1;
+    } else {
+      half = 0;
+      r0 = rb0 + (t - na) * rpb;
+      r1 = rb1;
+    }
+  };
+  auto fetch = [&](int t) {
+    t = imin(t, nblk - 1);
+    int half, r0, r1;
+    block_row0(t, half, r0, r1);
+#pragma unroll
+    for (int u = 0; u < QU; ++u) {
+      const int ch = tid + u * NT;
+      qreg[u] = dreg[u] = u32x4{0, 0, 0, 0};
+      if (QCH % NT == 0 || ch < QCH) {
+        const int sl_ = ch / CPR, c = ch % CPR;
+        const int rl = sl_ / a.G, pos = r0 + rl;
+        if (rl < rpb && pos < r1) {
+          const int head = g * a.G + (sl_ - rl * a.G);
+          const size_t off = ((size_t)(b * a.Hq + head) * a.S + half * a.L + pos) * D + 8 * c;
+          qreg[u] = *(const u32x4*)(a.q + off);
+          dreg[u] = *(const u32x4*)(a.dout + off);
+        }
+      }
+    }
+    if (tid < 32) {
+      const int rl = tid / a.G, pos = r0 + rl;
+      slv[0] = INFINITY;
+      slv[1] = 0.f;
+      srv = -1;
+      if (rl < rpb && pos < r1) {
+        const int head = g * a.G + (tid - rl * a.G);
+        const size_t ri = (size_t)(b * a.Hq + head) * a.S + half * a.L + pos;
+        slv[0] = a.lse[ri] * kLn2Inv;
+        slv[1] = a.delta[ri];
+        srv = half * a.L + pos;
+      }
+    }
+  };
+  auto lstore = [&](int st) {
+#pragma unroll
+    for (int u = 0; u < QU; ++u) {
+      const int ch = tid + u * NT;
+      if (QCH % NT == 0 || ch < QCH) {
+        const int off = chunk_off<D>(ch / CPR, ch % CPR);
+        *(u32x4*)(&qd[st][off]) = qreg[u];
+        *(u32x4*)(&qd[st][QE + off]) = dreg[u];
+      }
+    }
+    if (tid < 32) {
+      sl[st][0][tid] = slv[0];
+      sl[st][1][tid] = slv[1];
+      srow[st][tid] = srv;
+    }
+  };
+
+  // lane constants: my key, and the transpose-read offsets
+  const int key = kp0 + 32 * w + ql;            // position of my key in its half
+  const bool key_ok = key < kp1;
+  const int kj = (clean ? a.L : 0) + key;       // key-tensor row of my key
+  const int kr_off = (32 * w + ql) * D;          // my key's row in the K / V tile
+  const int k_swz = swz<D>(32 * w + ql) & (CPR - 1);
+  const int q_swz = swz<D>(ql) & (CPR - 1);
+  int t_lo[DT], t_hi[DT];
+  {
+    const int jx = lane & 15, gi = lane >> 4;
+    const int r = 4 * hb + (jx >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int dcol = 32 * dt + 16 * (gi & 1) + 4 * (jx & 3);
+      t_lo[dt] = chunk_off<D>(r, dcol >> 3) + (dcol & 7);
+      t_hi[dt] = chunk_off<D>(r + 8, dcol >> 3) + (dcol & 7);
+    }
+  }
+
+  f32x16 dka[DT], dva[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dka[dt] = dva[dt] = f32x16{};
+
+  auto compute = [&](int st) {
+    const uint16_t* qb = &qd[st][0];
+    const uint16_t* db = &qd[st][QE];
+    f32x16 sv{}, dp{};
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const bf16x8 qa = *(const bf16x8*)(qb + ql * D + 8 * ((2 * ks + hb) ^ q_swz));
+      const bf16x8 da = *(const bf16x8*)(db + ql * D + 8 * ((2 * ks + hb) ^ q_swz));
+      const bf16x8 kb = *(const bf16x8*)(kv + kr_off + 8 * ((2 * ks + hb) ^ k_swz));
+      const bf16x8 vb = *(const bf16x8*)(kv + KE + kr_off + 8 * ((2 * ks + hb) ^ k_swz));
+      sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb, sv, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vb, dp, 0, 0, 0);
+    }
+    // lane = key (column), value i = slot 8*(i/4) + 4*hb + (i%4)
+    f32x4 l4[4], d4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      l4[u] = *(const f32x4*)(&sl[st][0][8 * u + 4 * hb]);
+      d4[u] = *(const f32x4*)(&sl[st][1][8 * u + 4 * hb]);
+    }
+    bf16x8 pb[2], sb[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      u32x4 pk, dk4;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        float pv[2], dv2[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int i = 8 * kk + 2 * e2 + h;
+          const int slot = 8 * (i >> 2) + 4 * hb + (i & 3);
+          const int row = srow[st][slot];
+          bool ok = key_ok && row >= 0;
+          if (ok) {
+            Span A, C;
+            row_spans(kHybrid, a.L, 2 * a.L, a.blk, row, A, C);
+            ok = in_span(A, kj) || in_span(C, kj);
+          }
+          const float p = ok ? exp2_fast(fmaf(sv[i], a.sl2, -l4[i >> 2][i & 3])) : 0.f;
+          pv[h] = p;
+          dv2[h] = p * (dp[i] - d4[i >> 2][i & 3]);
+        }
+        pk[e2] = pack_bf16x2(pv[0], pv[1]);
+        dk4[e2] = pack_bf16x2(dv2[0], dv2[1]);
+      }
+      pb[kk] = __builtin_bit_cast(bf16x8, pk);
+      sb[kk] = __builtin_bit_cast(bf16x8, dk4);
+    }
+    // dV += P^T dO, dK += dS^T Q (slots {16kk + 4hb + 0..3, +8} by transpose reads)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const s16x4 dlo = lds_read_tr(db + 16 * kk * D + t_lo[dt]);
+        const s16x4 dhi = lds_read_tr(db + 16 * kk * D + t_hi[dt]);
+        const s16x4 qlo = lds_read_tr(qb + 16 * kk * D + t_lo[dt]);
+        const s16x4 qhi = lds_read_tr(qb + 16 * kk * D + t_hi[dt]);
+        const bf16x8 dop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 qop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
+        dva[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb[kk], dop, dva[dt], 0, 0, 0);
+        dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sb[kk], qop, dka[dt], 0, 0, 0);
+      }
+    }
+  };
+
+  if (nblk > 0) {
+    fetch(0);
+    lstore(0);
+    fetch(1);
+    __syncthreads();
+#pragma unroll 1
+    for (int t = 0; t < nblk; ++t) {
+      const int st = t & 1;
+      compute(st);
+      lstore(st ^ 1);
+      fetch(t + 2);
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+
+  // write dK (scaled) and dV: accumulator lane (ql, hb) holds column
+  // d = 32*dt + ql and keys 8*(i/4) + 4*hb + (i%4) of the wavefront's 32;
+  // transposed through LDS into 16-byte rows
+  uint16_t* tk = kv + w * 2 * 32 * D;           // this wavefront's 2 x [32 keys][D]
+  uint16_t* tv = tk + 32 * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kr = 8 * (i >> 2) + 4 * hb + (i & 3);
+      tk[kr * D + 32 * dt + ql] = __builtin_bit_cast(uint16_t, (__bf16)(dka[dt][i] * a.scale));
+      tv[kr * D + 32 * dt + ql] = __builtin_bit_cast(uint16_t, (__bf16)dva[dt][i]);
+    }
+  __syncthreads();
+  for (int ch = lane; ch < 32 * CPR; ch += 64) {
+    const int kr = ch / CPR, c = ch % CPR;
+    const int kpos = kp0 + 32 * w + kr;
+    if (kpos < kp1) {
+      const size_t off = kvoff + (size_t)((clean ? a.L : 0) + kpos) * D + 8 * c;
+      *(u32x4*)(a.dk + off) = *(const u32x4*)(tk + kr * D + 8 * c);
+      *(u32x4*)(a.dv + off) = *(const u32x4*)(tv + kr * D + 8 * c);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+
+int bwd_make_plan(int B, int Hq, int Hkv, int L, int d, int block, BwdPlan* p, const char** why) {
+  BwdPlan x{};
+  x.B = B;
+  x.Hq = Hq;
+  x.Hkv = Hkv;
+  x.G = Hq / Hkv;
+  x.L = L;
+  x.blk = block;
+  x.d = d;
+  x.nw = L >= 256 ? 8 : 4;
+  if (x.G > (x.nw / 2) * 32 || x.G > 32) {
+    *why = "Hq/Hkv larger than 32 is not supported by the backward";
+    return 2;
+  }
+  x.rows_per_wg = ((x.nw / 2) * 32) / x.G;
+  x.n_qtiles = (L + x.rows_per_wg - 1) / x.rows_per_wg;
+  x.nkh = (L + 127) / 128;
+  const long long pairs = (long long)B * Hkv;
+  x.pairs_per_xcd = pairs % 8 == 0 ? (int)(pairs / 8) : 0;
+  x.grid_dq = pairs * x.n_qtiles;
+  x.grid_kv = pairs * 2 * x.nkh;
+  if (x.grid_dq > 0x7fffffffLL || x.grid_kv > 0x7fffffffLL) {
+    *why = "grid too large";
+    return 2;
+  }
+  x.ws_bytes = (size_t)B * Hq * 2 * (size_t)L * 4;
+  *p = x;
+  return 0;
+}
+
+template <int D>
+static hipError_t bwd_launch_d(const BwdPlan& p, const BwdArgs& a, hipStream_t st) {
+  const long long rows = (long long)p.B * p.Hq * 2 * p.L;
+  const long long blocks = (rows * (D / 8) + 255) / 256;
+  hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, st, a.o, a.dout, a.delta,
+                     rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.nw == 8)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, 8>), dim3((unsigned)p.grid_dq), dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, 4>), dim3((unsigned)p.grid_dq), dim3(256), 0, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)p.grid_kv), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t bwd_launch(const BwdPlan& p, const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv, void* ws,
+                      hipStream_t st) {
+  BwdArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.o = (const uint16_t*)o;
+  a.dout = (const uint16_t*)dout;
+  a.lse = lse;
+  a.delta = (float*)ws;
+  a.dq = (uint16_t*)dq;
+  a.dk = (uint16_t*)dk;
+  a.dv = (uint16_t*)dv;
+  a.B = p.B;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.G = p.G;
+  a.L = p.L;
+  a.blk = p.blk;
+  a.S = 2 * p.L;
+  a.rows_per_wg = p.rows_per_wg;
+  a.n_qtiles = p.n_qtiles;
+  a.nkh = p.nkh;
+  a.pairs_per_xcd = p.pairs_per_xcd;
+  a.scale = 1.f / sqrtf((float)p.d);
+  a.sl2 = 1.4426950408889634f * a.scale;
+  (void)hipGetLastError();
+  switch (p.d) {
+    case 32: return bwd_launch_d<32>(p, a, st);
+    case 64: return bwd_launch_d<64>(p, a, st);
+    default: return bwd_launch_d<128>(p, a, st);
+  }
+}
+
+}  // namespace bda

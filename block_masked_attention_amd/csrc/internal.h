@@ -45,4 +45,21 @@ hipError_t stats_launch(const CommitPlan& p, const void* logits, const uint8_t* 
 hipError_t verify_launch(const CommitPlan& p, const void* logits, const int64_t* drafts,
                          int64_t* argmax_out, int32_t* accept, void* ws, hipStream_t st);
 
+// Backward of the training form (hybrid mask).
+struct BwdPlan {
+  int B, Hq, Hkv, G, L, blk, d;
+  int nw;               // wavefronts of the dq workgroup
+  int rows_per_wg;      // dq: query rows per tile (per half)
+  int n_qtiles;         // dq: query tiles per (batch, kv head)
+  int nkh;              // dkdv: 128-key tiles per half
+  int pairs_per_xcd;    // >0: XCD-aware order
+  long long grid_dq, grid_kv;
+  size_t ws_bytes;      // per-row delta = rowsum(dO * O), fp32
+};
+
+int bwd_make_plan(int B, int Hq, int Hkv, int L, int d, int block, BwdPlan* p, const char** why);
+hipError_t bwd_launch(const BwdPlan& p, const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv, void* ws,
+                      hipStream_t st);
+
 }  // namespace bda

@@ -96,6 +96,26 @@ int bda_attn_fwd_lse(const void* q, const void* k, const void* v, void* out, flo
                      void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Backward of the training form (mode must be BDA_MODE_HYBRID; others return
+ * BDA_EUNSUPPORTED) ([NLD-3x] sec. 1 mask; the [LLaDA] BDLM objective trains
+ * through it).  For loss = sum(dout * out) with out = bda_attn_fwd(q, k, v):
+ *   dq = d loss / d q, dk = d loss / d k, dv = d loss / d v,
+ * where the G = Hq/Hkv query heads of a kv head add into its dk, dv.
+ * q, out, dout, dq: [B, Hq, 2L, d] bf16; k, v, dk, dv: [B, Hkv, 2L, d] bf16;
+ * lse: [B, Hq, 2L] fp32 as written by bda_attn_fwd_lse for the same inputs.
+ * Hq/Hkv <= 32.  All device pointers 16-byte aligned; the gradients must not
+ * overlap the inputs or each other.  fp32 accumulation; the softmax is
+ * rebuilt exactly from lse.
+ * workspace: at least bda_attn_bwd_workspace_bytes(...) bytes (per-row
+ *   rowsum(dout * out), fp32); no initial contents are required.
+ */
+int bda_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv,
+                 int B, int Hq, int Hkv, int L, int d, int block, int mode,
+                 void* workspace, size_t ws_bytes, void* stream);
+size_t bda_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int block, int mode);
+
+/*
  * Confidence commit ([LLaDA] SPRINT; [DGemma] Schedulers; [VLM-8B]).
  * logits: [G, R, V] of dtype BDA_BF16 or BDA_F32 (G independent groups, e.g.
  *   sequences; R canvas positions; V vocabulary).  Values must be finite.
