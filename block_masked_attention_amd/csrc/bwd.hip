@@ -19,6 +19,8 @@
 //          dK += dS^T Q (dO and Q by the LDS transpose read).
 // P is rebuilt exactly from the log-sum-exp (no running max); masked pairs
 // get P = 0.  fp32 accumulation, bf16 MFMA operands, bf16 gradients.
+#include <limits.h>
+
 #include "common.h"
 #include "geometry.h"
 #include "internal.h"
@@ -288,11 +290,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   constexpr int KE = TK * D;                   // elements of the K (or V) tile
   constexpr int QE = 32 * D;                   // elements of a Q (or dO) block
   constexpr int QCH = 32 * CPR;                // chunks of a Q block
-  constexpr int QU = (QCH + NT - 1) / NT;      // chunks per thread per matrix
   __shared__ __attribute__((aligned(16))) uint16_t kv[2 * KE];
-  __shared__ __attribute__((aligned(16))) uint16_t qd[2][2 * QE];
-  __shared__ __attribute__((aligned(16))) float sl[2][2][32];   // lse2, delta per slot
-  __shared__ int srow[2][32];                                   // query row of each slot, -1 if none
+  constexpr int NS = 4;                        // query-block stages, filled three blocks ahead
+  __shared__ __attribute__((aligned(16))) uint16_t qd[NS][2 * QE];
+  __shared__ __attribute__((aligned(16))) float sl[NS][2][32];  // lse (natural log), delta per slot
+  // Per slot, the mask as one integer t: clean-key tiles let a slot see key
+  // block kb iff kb <= t (t = the row's block for an x_0 row, one less for
+  // an x_t row); noisy-key tiles iff kb == t (t = the row's block for an
+  // x_t row).  t = -1: no such row, or a row that sees nothing of the tile.
+  __shared__ __attribute__((aligned(16))) int sthr[NS][32];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, ql = lane & 31, hb = lane >> 5;
   const int nk = 2 * a.nkh;
@@ -351,10 +357,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   const int nb = rb1 > rb0 ? (rb1 - rb0 + rpb - 1) / rpb : 0;
   const int nblk = na + nb;
 
-  // staging of block t: Q and dO chunks through registers
-  u32x4 qreg[QU], dreg[QU];
-  float slv[2];
-  int srv = -1;
+  // Block t of query slots straight from global memory into LDS stage st:
+  // Q and dO rows (each lane loads the 16-byte chunk the permuted layout puts
+  // at its lane slot), then the slots' lse and delta (one dword per lane of
+  // lanes 0..15 of every wavefront: dwords 16w .. 16w+15 of lse[32] ++
+  // delta[32]).  Slots without a row load row 0 of the block (finite data
+  // the thresholds never let through).  Every wavefront issues the same
+  // number of loads, so one vmcnt bound serves all.
+  constexpr int QRUNS = QCH / 64;                         // 64-chunk runs of a Q block
+  constexpr int QJ = (QRUNS + 3) / 4;                     // runs per wavefront per matrix
   auto block_row0 = [&](int t, int& half, int& r0, int& r1) {
     if (t < na) {
       half = ha;
@@ -366,60 +377,66 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
       r1 = rb1;
     }
   };
-  auto fetch = [&](int t) {
-    t = imin(t, nblk - 1);
+  const unsigned lds_qd = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)&qd[0][0]);
+  const unsigned lds_sl = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)&sl[0][0][0]);
+  auto issue = [&](int t, int st) {
+    t = imin(t, nblk - 1);                      // past the end: repeat the last block (never computed)
     int half, r0, r1;
     block_row0(t, half, r0, r1);
 #pragma unroll
-    for (int u = 0; u < QU; ++u) {
-      const int ch = tid + u * NT;
-      qreg[u] = dreg[u] = u32x4{0, 0, 0, 0};
-      if (QCH % NT == 0 || ch < QCH) {
-        const int sl_ = ch / CPR, c = ch % CPR;
-        const int rl = sl_ / a.G, pos = r0 + rl;
-        if (rl < rpb && pos < r1) {
-          const int head = g * a.G + (sl_ - rl * a.G);
-          const size_t off = ((size_t)(b * a.Hq + head) * a.S + half * a.L + pos) * D + 8 * c;
-          qreg[u] = *(const u32x4*)(a.q + off);
-          dreg[u] = *(const u32x4*)(a.dout + off);
-        }
-      }
+    for (int q = 0; q < QJ; ++q) {
+      const int run = imin(w + 4 * q, QRUNS - 1);   // spare wavefronts repeat the last run
+      const int pos = run * 64 + lane;
+      const int sl_ = pos / CPR, c = (pos % CPR) ^ (swz<D>(sl_) & (CPR - 1));
+      const int rl = sl_ / a.G;
+      const bool ok = rl < rpb && r0 + rl < r1;
+      const int head = g * a.G + (ok ? sl_ - rl * a.G : 0);
+      const size_t off = ((size_t)(b * a.Hq + head) * a.S + half * a.L + (ok ? r0 + rl : r0)) * D + 8 * c;
+      const unsigned dst = lds_qd + (unsigned)(st * 2 * QE + run * 512) * 2;
+      lds_dma16s(a.q + off, dst);
+      lds_dma16s(a.dout + off, dst + QE * 2);
     }
-    if (tid < 32) {
+    {
+      const int x = 16 * w + (lane & 15);       // dword of lse[32] ++ delta[32]
+      const int slot = x & 31;
+      const int rl = slot / a.G;
+      const bool ok = rl < rpb && r0 + rl < r1;
+      const int head = g * a.G + (ok ? slot - rl * a.G : 0);
+      const size_t ri = (size_t)(b * a.Hq + head) * a.S + half * a.L + (ok ? r0 + rl : r0);
+      const float* src = (x < 32 ? a.lse : a.delta) + ri;
+      if (lane < 16) lds_dma4s(src, lds_sl + (unsigned)(st * 64 + 16 * w) * 4);
+    }
+    if (tid < 32) {                             // the slots' mask thresholds
       const int rl = tid / a.G, pos = r0 + rl;
-      slv[0] = INFINITY;
-      slv[1] = 0.f;
-      srv = -1;
+      int t_ = -1;
       if (rl < rpb && pos < r1) {
-        const int head = g * a.G + (tid - rl * a.G);
-        const size_t ri = (size_t)(b * a.Hq + head) * a.S + half * a.L + pos;
-        slv[0] = a.lse[ri] * kLn2Inv;
-        slv[1] = a.delta[ri];
-        srv = half * a.L + pos;
+        const int rb = pos / a.blk;
+        t_ = clean ? (half == 1 ? rb : rb - 1) : (half == 0 ? rb : -1);
       }
+      sthr[st][tid] = t_;
     }
   };
-  auto lstore = [&](int st) {
-#pragma unroll
-    for (int u = 0; u < QU; ++u) {
-      const int ch = tid + u * NT;
-      if (QCH % NT == 0 || ch < QCH) {
-        const int off = chunk_off<D>(ch / CPR, ch % CPR);
-        *(u32x4*)(&qd[st][off]) = qreg[u];
-        *(u32x4*)(&qd[st][QE + off]) = dreg[u];
-      }
-    }
-    if (tid < 32) {
-      sl[st][0][tid] = slv[0];
-      sl[st][1][tid] = slv[1];
-      srow[st][tid] = srv;
-    }
+  auto settle = [&]() {
+    constexpr int N = 2 * QJ + 1;               // this block's loads stay in flight
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  auto drain = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
 
   // lane constants: my key, and the transpose-read offsets
   const int key = kp0 + 32 * w + ql;            // position of my key in its half
   const bool key_ok = key < kp1;
-  const int kj = (clean ? a.L : 0) + key;       // key-tensor row of my key
+  const int kblk = key_ok ? key / a.blk : INT_MAX / 2;   // my key's block (past the end: never seen)
+  // the wavefront's key blocks, for whole-block decisions
+  const int wk0 = kp0 + 32 * w, wk1 = imin(kp1, wk0 + 32);
+  const int wb0 = wk0 / a.blk, wb1 = wk1 > wk0 ? (wk1 - 1) / a.blk : -1;
   const int kr_off = (32 * w + ql) * D;          // my key's row in the K / V tile
   const int k_swz = swz<D>(32 * w + ql) & (CPR - 1);
   const int q_swz = swz<D>(ql) & (CPR - 1);
@@ -435,6 +452,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     }
   }
 
+  bf16x8 kop[KSTEPS], vop[KSTEPS];              // my key's K and V operands (read once from LDS)
   f32x16 dka[DT], dva[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dka[dt] = dva[dt] = f32x16{};
@@ -442,22 +460,35 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   auto compute = [&](int st) {
     const uint16_t* qb = &qd[st][0];
     const uint16_t* db = &qd[st][QE];
+    // whole-block decision from the 32 slot thresholds (uniform per wave)
+    const int my_t = sthr[st][ql];
+    bool any_seen, all_seen;
+    if (wk1 <= wk0) {
+      any_seen = all_seen = false;
+    } else if (clean) {
+      any_seen = __any(my_t >= wb0);
+      all_seen = __all(my_t >= wb1) && wk1 - wk0 == 32;
+    } else {
+      any_seen = __any(my_t >= wb0 && my_t <= wb1);
+      all_seen = wb0 == wb1 && __all(my_t == wb0) && wk1 - wk0 == 32;
+    }
+    if (!any_seen) return;
     f32x16 sv{}, dp{};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       const bf16x8 qa = *(const bf16x8*)(qb + ql * D + 8 * ((2 * ks + hb) ^ q_swz));
       const bf16x8 da = *(const bf16x8*)(db + ql * D + 8 * ((2 * ks + hb) ^ q_swz));
-      const bf16x8 kb = *(const bf16x8*)(kv + kr_off + 8 * ((2 * ks + hb) ^ k_swz));
-      const bf16x8 vb = *(const bf16x8*)(kv + KE + kr_off + 8 * ((2 * ks + hb) ^ k_swz));
-      sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb, sv, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vb, dp, 0, 0, 0);
+      sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kop[ks], sv, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vop[ks], dp, 0, 0, 0);
     }
     // lane = key (column), value i = slot 8*(i/4) + 4*hb + (i%4)
     f32x4 l4[4], d4[4];
+    i32x4 t4[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      l4[u] = *(const f32x4*)(&sl[st][0][8 * u + 4 * hb]);
+      l4[u] = *(const f32x4*)(&sl[st][0][8 * u + 4 * hb]) * kLn2Inv;
       d4[u] = *(const f32x4*)(&sl[st][1][8 * u + 4 * hb]);
+      t4[u] = *(const i32x4*)(&sthr[st][8 * u + 4 * hb]);
     }
     bf16x8 pb[2], sb[2];
 #pragma unroll
@@ -469,14 +500,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int i = 8 * kk + 2 * e2 + h;
-          const int slot = 8 * (i >> 2) + 4 * hb + (i & 3);
-          const int row = srow[st][slot];
-          bool ok = key_ok && row >= 0;
-          if (ok) {
-            Span A, C;
-            row_spans(kHybrid, a.L, 2 * a.L, a.blk, row, A, C);
-            ok = in_span(A, kj) || in_span(C, kj);
-          }
+          const int t = t4[i >> 2][i & 3];
+          const bool ok = all_seen || (clean ? kblk <= t : kblk == t);
           const float p = ok ? exp2_fast(fmaf(sv[i], a.sl2, -l4[i >> 2][i & 3])) : 0.f;
           pv[h] = p;
           dv2[h] = p * (dp[i] - d4[i >> 2][i & 3]);
@@ -505,20 +530,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   };
 
   if (nblk > 0) {
-    fetch(0);
-    lstore(0);
-    fetch(1);
-    __syncthreads();
+    issue(0, 0);
+    issue(1, 1);
+    issue(2, 2);
+    drain();
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      kop[ks] = *(const bf16x8*)(kv + kr_off + 8 * ((2 * ks + hb) ^ k_swz));
+      vop[ks] = *(const bf16x8*)(kv + KE + kr_off + 8 * ((2 * ks + hb) ^ k_swz));
+    }
 #pragma unroll 1
     for (int t = 0; t < nblk; ++t) {
-      const int st = t & 1;
-      compute(st);
-      lstore(st ^ 1);
-      fetch(t + 2);
-      __syncthreads();
+      issue(t + 3, (t + 3) % NS);
+      compute(t % NS);
+      settle();
     }
   }
-  __syncthreads();
+  drain();
 
   // write dK (scaled) and dV: accumulator lane (ql, hb) holds column
   // d = 32*dt + ql and keys 8*(i/4) + 4*hb + (i%4) of the wavefront's 32;

@@ -46,6 +46,17 @@ __device__ __forceinline__ void lds_dma16(const uint16_t* g, const uint16_t* lds
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(base) : "memory");
 }
 
+// The same with the run starting at LDS byte address m0 (uniform).
+__device__ __forceinline__ void lds_dma16s(const uint16_t* g, unsigned m0) {
+  m0 = __builtin_amdgcn_readfirstlane(m0);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory");
+}
+// 4 bytes per lane: lane i writes LDS byte address m0 + 4*i.
+__device__ __forceinline__ void lds_dma4s(const float* g, unsigned m0) {
+  m0 = __builtin_amdgcn_readfirstlane(m0);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory");
+}
+
 // ds_read_b64_tr_b16: within each 16-lane group, lane j receives element
 // (j & 3) of the 4-element row read by lane 4*e + (j >> 2), for e = 0..3.
 __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
