@@ -55,6 +55,8 @@ def _load():
     lib.oracle_verify.argtypes = [P, P, P, P, L, L, L, I]
     lib.oracle_row_stats.argtypes = [P, P, P, P, P, P, L, L, L, I]
     lib.oracle_attention_bwd.argtypes = [I, P, P, P, P, P, P, P, P, L, L, L, L, L, L, I]
+    lib.oracle_sprint.argtypes = [P, P, P, ctypes.c_double, ctypes.c_double, ctypes.c_double, L, L, L, L, P, P]
+    lib.oracle_sprint.restype = L
     lib.oracle_max_threads.restype = I
     for f in (lib.oracle_mask_shape, lib.oracle_mask, lib.oracle_attention,
               lib.oracle_commit, lib.oracle_verify, lib.oracle_row_stats, lib.oracle_attention_bwd):
@@ -127,6 +129,24 @@ def attention_bwd(mode: str, q, k, v, dout, L: int, block: int, nthreads: int = 
     if rc:
         raise ValueError("oracle_attention_bwd: bad arguments")
     return dq, dk, dv, lse
+
+
+def sprint(k, conf, modality, alpha: float = 0.5, r_img: float = 0.8, r_text: float = 1.0):
+    """SPRINT prefix retention in double: (kept [B, L] int64, -1 padded;
+    scores [B, L] float64; K kept positions per batch)."""
+    lib = _load()
+    kk = _f32(k)
+    B, Hkv, L, d = kk.shape
+    cf = np.ascontiguousarray(np.asarray(conf, dtype=np.float32).reshape(B, L))
+    md = np.ascontiguousarray(np.asarray(modality, dtype=np.uint8).reshape(L))
+    kept = np.empty((B, L), dtype=np.int64)
+    sc = np.empty((B, L), dtype=np.float64)
+    # the ratios are fp32 parameters (as the library takes them); counts use their double values
+    K = lib.oracle_sprint(_ptr(kk), _ptr(cf), _ptr(md), float(np.float32(alpha)), float(np.float32(r_img)),
+                          float(np.float32(r_text)), B, Hkv, L, d, _ptr(kept), _ptr(sc))
+    if K < 0:
+        raise ValueError("oracle_sprint: bad arguments")
+    return kept, sc, int(K)
 
 
 def commit(logits, masked, tokens, threshold: float, k_min: int, nthreads: int = 0):

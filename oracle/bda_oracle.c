@@ -491,6 +491,67 @@ int oracle_row_stats(const float* logits, const uint8_t* masked, double* conf, i
     return 0;
 }
 
+/*
+ * SPRINT sparse prefix retention ([LLaDA] "SPRINT": the cache is pruned once
+ * at the start of a block).  For batch b and prefix position i:
+ *   n_i   = || k_{b,.,i,.} ||_2 over all kv heads and channels,
+ *   I_i   = n_i / ((1/L) sum_j n_j)                 (mean-normalised key norm),
+ *   s_i   = alpha * I_i + (1 - alpha) * conf[b,i]    (composite score),
+ * then, separately for image positions (modality 1) and text positions (0),
+ * the keep_m = floor(r_m * count_m + 0.5) positions with the largest s_i are
+ * kept (ties: lower position first).  kept[b, 0..K) lists the kept positions
+ * in increasing order, -1 after; scores[b, i] = s_i.  Returns K (the same
+ * for every batch), or -1 on a bad argument.
+ */
+long oracle_sprint(const float* k, const float* conf, const uint8_t* modality, double alpha, double r_img,
+                   double r_text, long B, long Hkv, long L, long d, int64_t* kept, double* scores)
+{
+    if (B <= 0 || Hkv <= 0 || L <= 0 || d <= 0) return -1;
+    long cnt[2] = {0, 0};
+    for (long i = 0; i < L; ++i) cnt[modality[i] ? 1 : 0]++;
+    const long keep[2] = {(long)floor(r_text * (double)cnt[0] + 0.5), (long)floor(r_img * (double)cnt[1] + 0.5)};
+    if (keep[0] < 0 || keep[0] > cnt[0] || keep[1] < 0 || keep[1] > cnt[1]) return -1;
+    double* nrm = (double*)malloc(sizeof(double) * (size_t)L);
+    long* order = (long*)malloc(sizeof(long) * (size_t)L);
+    uint8_t* take = (uint8_t*)malloc((size_t)L);
+    if (!nrm || !order || !take) { free(nrm); free(order); free(take); return -1; }
+    for (long b = 0; b < B; ++b) {
+        double mean = 0.0;
+        for (long i = 0; i < L; ++i) {
+            double ss = 0.0;
+            for (long h = 0; h < Hkv; ++h)
+                for (long c = 0; c < d; ++c) {
+                    const double x = (double)k[((b * Hkv + h) * L + i) * d + c];
+                    ss += x * x;
+                }
+            nrm[i] = sqrt(ss);
+            mean += nrm[i];
+        }
+        mean /= (double)L;
+        double* sc = scores + b * L;
+        for (long i = 0; i < L; ++i)
+            sc[i] = alpha * (nrm[i] / mean) + (1.0 - alpha) * (double)conf[b * L + i];
+        for (long i = 0; i < L; ++i) take[i] = 0;
+        for (int m = 0; m < 2; ++m) {
+            /* selection: repeatedly take the best remaining position of modality m */
+            for (long t = 0; t < keep[m]; ++t) {
+                long best = -1;
+                for (long i = 0; i < L; ++i) {
+                    if ((modality[i] ? 1 : 0) != m || take[i]) continue;
+                    if (best < 0 || sc[i] > sc[best]) best = i;
+                }
+                take[best] = 1;
+            }
+        }
+        long K = 0;
+        for (long i = 0; i < L; ++i)
+            if (take[i]) kept[b * L + K++] = i;
+        for (long j = K; j < L; ++j) kept[b * L + j] = -1;
+    }
+    free(nrm); free(order); free(take);
+    return keep[0] + keep[1];
+}
+
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP

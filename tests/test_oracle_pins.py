@@ -464,3 +464,66 @@ def test_attention_bwd_zero_upstream_rows_send_nothing_to_their_private_keys():
     _, dk, dv, _ = oracle.attention_bwd(mode, q, k, v, do, L, blk)
     assert np.abs(dk[:, :, 2:4]).max() == 0.0 and np.abs(dv[:, :, 2:4]).max() == 0.0
     assert np.abs(dk[:, :, 4:6]).max() > 0.0
+
+
+# ---- SPRINT sparse prefix retention ([LLaDA] SPRINT)
+
+def _sprint_brute(k, conf, modality, alpha, r_img, r_text):
+    """Pure-Python restatement on tiny inputs: norms by loops, then a sort by
+    (score descending, position ascending) per modality."""
+    B, H, L, d = k.shape
+    r = {1: float(np.float32(r_img)), 0: float(np.float32(r_text))}
+    a = float(np.float32(alpha))
+    out = []
+    for b in range(B):
+        n = [math.sqrt(sum(float(k[b, h, i, c]) ** 2 for h in range(H) for c in range(d))) for i in range(L)]
+        mean = sum(n) / L
+        s = [a * n[i] / mean + (1 - a) * float(conf[b, i]) for i in range(L)]
+        keep = set()
+        for m in (0, 1):
+            pos = [i for i in range(L) if int(modality[i]) == m]
+            cnt = math.floor(r[m] * len(pos) + 0.5)
+            keep.update(sorted(pos, key=lambda i: (-s[i], i))[:cnt])
+        out.append(sorted(keep))
+    return out
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_sprint_brute_force(seed):
+    g = np.random.default_rng(40 + seed)
+    B, H, L, d = 2, 2, 37, 5
+    k = g.standard_normal((B, H, L, d)).astype(np.float32) * g.uniform(0.2, 3.0, (1, 1, L, 1)).astype(np.float32)
+    conf = g.uniform(0, 1, (B, L)).astype(np.float32)
+    mod = (g.uniform(size=L) < 0.6).astype(np.uint8)
+    kept, sc, K = oracle.sprint(k, conf, mod, 0.5, 0.8, 1.0)
+    ref = _sprint_brute(k, conf, mod, 0.5, 0.8, 1.0)
+    for b in range(B):
+        assert list(kept[b, :K]) == ref[b] and (kept[b, K:] == -1).all()
+
+
+def test_sprint_equal_norms_rank_by_confidence_and_ratios():
+    L, d = 40, 8
+    base = np.arange(1, d + 1, dtype=np.float32)
+    k = np.stack([np.roll(base, i) for i in range(L)])[None, None]      # every key has the same norm
+    conf = np.linspace(0.0, 1.0, L, dtype=np.float32)[::-1].copy()[None]  # position 0 most confident
+    mod = np.array([1] * 30 + [0] * 10, dtype=np.uint8)
+    kept, sc, K = oracle.sprint(k, conf, mod, 0.5, 0.8, 1.0)
+    assert np.allclose(sc, 0.5 + 0.5 * conf.astype(np.float64), rtol=1e-12)   # I_i = 1
+    assert K == 24 + 10 and list(kept[0, :K]) == list(range(24)) + list(range(30, 40))
+    kept1, _, K1 = oracle.sprint(k, conf, mod, 0.5, 1.0, 1.0)
+    assert K1 == L and list(kept1[0]) == list(range(L))
+    kept0, _, K0 = oracle.sprint(k, conf, mod, 0.5, 0.0, 1.0)
+    assert K0 == 10 and list(kept0[0, :K0]) == list(range(30, 40))
+
+
+def test_sprint_equal_confidence_ranks_by_key_norm():
+    L = 16
+    k = np.zeros((1, 2, L, 4), np.float32)
+    norms = np.array([3, 1, 4, 1, 5, 9, 2, 6, 5, 3, 5, 8, 9, 7, 9, 3], np.float32)
+    k[0, 0, :, 0] = norms                                                 # one kv head carries the norm
+    mod = np.ones(L, np.uint8)
+    kept, sc, K = oracle.sprint(k, np.full((1, L), 0.4, np.float32), mod, 0.5, 0.5, 1.0)
+    n64 = norms.astype(np.float64)
+    assert np.allclose(sc[0], 0.5 * n64 / n64.mean() + 0.5 * float(np.float32(0.4)), rtol=1e-12)
+    order = sorted(range(L), key=lambda i: (-norms[i], i))[:K]
+    assert K == 8 and list(kept[0, :K]) == sorted(order)                  # ties (the 9s, 5s) by position
