@@ -357,6 +357,37 @@ def secondary(bda, synth, torch, dev, args):
                         "algorithmic_bytes": byts}
     log(f"[bench] row_stats: {res['row_stats']}")
 
+    # ---- SPRINT pruning of the multimodal prefix (B=2, 8 kv heads, 4096
+    # positions: 3080 image, 1016 text; keep 0.8 of the image, all text), and
+    # one decode step of a 28-row block over the pruned vs the full cache.
+    pk, pv, pconf = synth.sprint_prefix()
+    pmod = synth.prefix_modality()
+    n_text = int((pmod == 0).sum())
+    pk, pv, pconf, pmod = pk.to(dev), pv.to(dev), pconf.to(dev), pmod.to(dev)
+    B, Hkv, L, d = pk.shape
+    spws = torch.empty(bda.lib.bda_sprint_workspace_bytes(B, L), dtype=torch.uint8, device=dev)
+    t_pr, _ = time_launches(lambda i: bda.sprint_prune(pk, pv, pconf, pmod, workspace=spws, n_text=n_text), iters, 5)
+    ko, vo, _, _ = bda.sprint_prune(pk, pv, pconf, pmod, workspace=spws, n_text=n_text)
+    K = ko.shape[2]
+    qs, kb, vb, _, _ = synth.multimodal_step(0, 28)
+    qs, kb, vb = qs.to(dev), kb.to(dev), vb.to(dev)
+    step_us = {}
+    for tag, (kk, vv) in (("full", (pk, pv)), ("pruned", (ko, vo))):
+        kc, vc = torch.cat([kk, kb], dim=2), torch.cat([vv, vb], dim=2)
+        out = torch.empty_like(qs)
+        ws = torch.empty(max(1, bda.attn_workspace_bytes(B, 32, Hkv, kc.shape[2], d, 28, "decode")),
+                         dtype=torch.uint8, device=dev)
+        t, _ = time_launches(lambda i: bda.attn_fwd(qs, kc, vc, "decode", 28, out=out, workspace=ws), iters, 5)
+        step_us[tag] = round(t * 1e3, 2)
+    byts = pk.numel() * 2 + 2 * 2 * B * Hkv * K * d * 2          # norms read K; gather reads and writes K and V rows
+    res["sprint_prune"] = {"B": B, "kv_heads": Hkv, "prefix": L, "kept": K, "us_per_call": round(t_pr * 1e3, 2),
+                           "hbm_floor_us": round(byts / PEAK_HBM_GBS / 1e3, 2),
+                           "decode_step_us_full_cache": step_us["full"],
+                           "decode_step_us_pruned_cache": step_us["pruned"]}
+    log(f"[bench] sprint_prune: {res['sprint_prune']}")
+    del pk, pv, pconf, pmod, ko, vo, spws
+    torch.cuda.empty_cache()
+
     # ---- verify on [16, 28, 131072] bf16
     vl, vidx, _ = synth.commit_logits(seed=6, G=16, R=28)
     drafts, _ = synth.verify_drafts(vidx)

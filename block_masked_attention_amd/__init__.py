@@ -25,7 +25,8 @@ _ENTRY_POINTS = (
     "bda_attn_fwd", "bda_attn_workspace_bytes", "bda_commit", "bda_commit_workspace_bytes",
     "bda_verify", "bda_verify_workspace_bytes", "bda_classify_tile", "bda_strerror",
     "bda_last_error", "bda_version", "bda_row_stats", "bda_row_stats_workspace_bytes",
-    "bda_attn_fwd_lse", "bda_attn_bwd", "bda_attn_bwd_workspace_bytes",
+    "bda_attn_fwd_lse", "bda_attn_bwd", "bda_attn_bwd_workspace_bytes", "bda_sprint_prune",
+    "bda_sprint_workspace_bytes", "bda_sprint_kept_count",
 )
 
 
@@ -63,6 +64,12 @@ def _load():
     L.bda_row_stats.restype = I
     L.bda_row_stats_workspace_bytes.argtypes = [I, I, I]
     L.bda_row_stats_workspace_bytes.restype = S
+    L.bda_sprint_prune.argtypes = [P, P, P, P, F, F, F, P, P, I, P, P, P, I, I, I, I, P, S, P]
+    L.bda_sprint_prune.restype = I
+    L.bda_sprint_workspace_bytes.argtypes = [I, I]
+    L.bda_sprint_workspace_bytes.restype = S
+    L.bda_sprint_kept_count.argtypes = [I, I, F, F]
+    L.bda_sprint_kept_count.restype = I
     L.bda_classify_tile.argtypes = [I, I, I, I, I, I, I]
     L.bda_classify_tile.restype = I
     for name in ("bda_strerror",):
@@ -252,6 +259,50 @@ def row_stats(logits, masked=None, workspace=None):
     if rc:
         raise BdaError(rc, "bda_row_stats")
     return conf, am, ent, mean
+
+
+def sprint_kept_count(n_image: int, n_text: int, r_img: float = 0.8, r_text: float = 1.0) -> int:
+    K = int(lib.bda_sprint_kept_count(n_image, n_text, r_img, r_text))
+    if K < 0:
+        raise ValueError("bad SPRINT counts or ratios")
+    return K
+
+
+def sprint_prune(k, v, conf, modality, alpha: float = 0.5, r_img: float = 0.8, r_text: float = 1.0,
+                 gather: bool = True, scores: bool = False, workspace=None, n_text=None):
+    """SPRINT prefix pruning of the cache k, v [B,Hkv,L,d] (bf16) with
+    per-position confidence ``conf`` (float32 [B,L]) and ``modality`` (uint8
+    [L], 0 = text).  Returns (k_out, v_out [B,Hkv,K,d] or None, kept int32
+    [B,L] (-1 padded), scores float32 [B,L] or None).  K is computed on the
+    host from the modality counts: pass ``n_text`` (the number of zeros in
+    ``modality``) when it is known, else it is read back from the device."""
+    for t in (k, v):
+        if t.dtype != torch.bfloat16 or t.dim() != 4:
+            raise ValueError("k, v must be 4-D bfloat16")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have one shape")
+    B, Hkv, L, d = k.shape
+    if conf.dtype != torch.float32 or tuple(conf.shape) != (B, L):
+        raise ValueError("conf must be float32 [B, L]")
+    if modality.dtype != torch.uint8 or tuple(modality.shape) != (L,):
+        raise ValueError("modality must be uint8 [L]")
+    dev = _check_dev(k, v, conf, modality)
+    if n_text is None:
+        n_text = int((modality == 0).sum().item())
+    K = sprint_kept_count(L - n_text, n_text, r_img, r_text)
+    cap = K if gather else 0
+    k_out = torch.empty((B, Hkv, cap, d), dtype=torch.bfloat16, device=dev) if gather else None
+    v_out = torch.empty((B, Hkv, cap, d), dtype=torch.bfloat16, device=dev) if gather else None
+    kept = torch.empty((B, L), dtype=torch.int32, device=dev)
+    sc = torch.empty((B, L), dtype=torch.float32, device=dev) if scores else None
+    need = int(lib.bda_sprint_workspace_bytes(B, L))
+    ws = _workspace(need, dev, workspace)
+    rc = lib.bda_sprint_prune(_ptr(k), _ptr(v), _ptr(conf), _ptr(modality), alpha, r_img, r_text,
+                              _ptr(k_out) if cap else None, _ptr(v_out) if cap else None, cap, _ptr(kept), None,
+                              _ptr(sc), B, Hkv, L, d, _ptr(ws), need, _stream(dev))
+    if rc:
+        raise BdaError(rc, "bda_sprint_prune")
+    return k_out, v_out, kept, sc
 
 
 def classify_tile(mode, L, block, q0, q1, k0, k1) -> int:

@@ -270,6 +270,47 @@ int bda_row_stats(const void* logits, int dtype, const uint8_t* masked, float* c
   return ok();
 }
 
+int bda_sprint_kept_count(int n_image, int n_text, float r_img, float r_text) {
+  if (n_image < 0 || n_text < 0 || !(r_img >= 0.f && r_img <= 1.f) || !(r_text >= 0.f && r_text <= 1.f)) return -1;
+  return bda::sprint_keep(n_image, r_img) + bda::sprint_keep(n_text, r_text);
+}
+
+size_t bda_sprint_workspace_bytes(int B, int L) {
+  if (B < 1 || L < 1) return 0;
+  return bda::sprint_ws_bytes(B, L);
+}
+
+int bda_sprint_prune(const void* k, const void* v, const float* conf, const uint8_t* modality, float alpha,
+                     float r_img, float r_text, void* k_out, void* v_out, int cap, int32_t* kept,
+                     int32_t* kept_count, float* scores, int B, int Hkv, int L, int d, void* workspace,
+                     size_t ws_bytes, void* stream) {
+  if (B < 1 || Hkv < 1 || L < 1) return fail(BDA_EINVAL, "B, Hkv and L must be >= 1");
+  if (d != 32 && d != 64 && d != 128) return fail(BDA_EUNSUPPORTED, "d must be 32, 64 or 128");
+  if (L > 16384) return fail(BDA_EUNSUPPORTED, "L above 16384 is not supported");
+  if (!(alpha >= 0.f && alpha <= 1.f) || !(r_img >= 0.f && r_img <= 1.f) || !(r_text >= 0.f && r_text <= 1.f))
+    return fail(BDA_EINVAL, "alpha, r_img and r_text must lie in [0, 1]");
+  if (cap < 0) return fail(BDA_EINVAL, "cap must be >= 0");
+  if (!k || !v || !conf || !modality || !kept) return fail(BDA_EINVAL, "k, v, conf, modality and kept must be non-NULL");
+  if (cap > 0 && (!k_out || !v_out)) return fail(BDA_EINVAL, "k_out and v_out must be non-NULL when cap > 0");
+  const void* al[] = {k, v, k_out, v_out};
+  for (const void* x : al)
+    if (x && !aligned16(x)) return fail(BDA_EINVAL, "k, v, k_out and v_out must be 16-byte aligned");
+  const size_t kb = (size_t)B * Hkv * L * d * 2, ob = (size_t)B * Hkv * cap * d * 2, lb = (size_t)B * L * 4;
+  if (cap > 0 && (overlap(k_out, ob, k, kb) || overlap(k_out, ob, v, kb) || overlap(v_out, ob, k, kb) ||
+                  overlap(v_out, ob, v, kb) || overlap(k_out, ob, v_out, ob)))
+    return fail(BDA_EINVAL, "k_out / v_out overlap k, v or each other");
+  if (overlap(kept, lb, k, kb) || overlap(kept, lb, v, kb) || (scores && overlap(scores, lb, kept, lb)))
+    return fail(BDA_EINVAL, "kept / scores overlap an input");
+  const size_t need = bda_sprint_workspace_bytes(B, L);
+  if (!workspace || ws_bytes < need)
+    return fail(BDA_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(BDA_EINVAL, "workspace must be 16-byte aligned");
+  hipError_t e = bda::sprint_launch(k, v, conf, modality, alpha, r_img, r_text, k_out, v_out, cap, kept, kept_count,
+                                    scores, B, Hkv, L, d, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BDA_EHIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int bda_classify_tile(int mode, int L, int block, int q0, int q1, int k0, int k1) {
   if (mode < 0 || mode > 2 || L < 1 || block < 1 || block > L) return -1;
   const int rows = mode == BDA_MODE_HYBRID ? 2 * L : block;

@@ -62,4 +62,13 @@ hipError_t bwd_launch(const BwdPlan& p, const void* q, const void* k, const void
                       const void* dout, const float* lse, void* dq, void* dk, void* dv, void* ws,
                       hipStream_t st);
 
+// SPRINT prefix retention.
+int sprint_keep(int n, float r);
+size_t sprint_lds_bytes(int L);
+size_t sprint_ws_bytes(int B, int L);
+hipError_t sprint_launch(const void* k, const void* v, const float* conf, const uint8_t* modality, float alpha,
+                         float r_img, float r_text, void* k_out, void* v_out, int cap, int32_t* kept,
+                         int32_t* kept_count, float* scores, int B, int Hkv, int L, int d, void* ws,
+                         hipStream_t st);
+
 }  // namespace bda

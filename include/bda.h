@@ -170,6 +170,39 @@ int bda_row_stats(const void* logits, int dtype, const uint8_t* masked, float* c
 size_t bda_row_stats_workspace_bytes(int G, int R, int V);
 
 /*
+ * SPRINT sparse prefix retention ([LLaDA] "SPRINT"): prune the clean KV
+ * prefix once, at the start of a block, to the positions that matter.
+ * k, v: [B, Hkv, L, d] bf16 (the prefix cache); conf: [B, L] float, each
+ * position's top-1 confidence (e.g. bda_row_stats' conf); modality: [L] uint8
+ * device array, 0 = text, nonzero = image (shared by the batch).
+ * Score of position i in batch b:
+ *   s = alpha * n_i / mean_j n_j + (1 - alpha) * conf[b, i],
+ * n_i = L2 norm of the position's keys over all Hkv heads (fp32).  Text
+ * positions keep the floor(r_text * n_text + 0.5) best scores and image
+ * positions the floor(r_img * n_image + 0.5) best, ties to the lower position.
+ * Outputs:
+ *   kept [B, L] int32: the kept positions in ascending order, then -1;
+ *   kept_count (int32, device, may be NULL): K, the kept count per batch
+ *     (equal in every batch; bda_sprint_kept_count gives it on the host);
+ *   scores [B, L] float (may be NULL): s;
+ *   k_out, v_out [B, Hkv, cap, d] bf16: rows 0..min(K, cap)-1 are the kept
+ *     rows of k and v in position order; rows from K on are not written.
+ *     cap = 0 skips the gather (k_out, v_out may then be NULL).
+ * alpha, r_img, r_text in [0, 1]; d in {32, 64, 128}; L <= 16384.
+ * k, v, k_out, v_out and the workspace must be 16-byte aligned, outputs must
+ * not overlap inputs.  workspace: bda_sprint_workspace_bytes(B, L) bytes.
+ * Three kernels on `stream`: key norms, selection, gather.
+ */
+int bda_sprint_prune(const void* k, const void* v, const float* conf, const uint8_t* modality,
+                     float alpha, float r_img, float r_text, void* k_out, void* v_out, int cap,
+                     int32_t* kept, int32_t* kept_count, float* scores, int B, int Hkv, int L, int d,
+                     void* workspace, size_t ws_bytes, void* stream);
+size_t bda_sprint_workspace_bytes(int B, int L);
+/* Host-only: the kept count K for n_image image and n_text text positions
+ * (-1 on bad arguments).  Touches no device. */
+int bda_sprint_kept_count(int n_image, int n_text, float r_img, float r_text);
+
+/*
  * Host-only tile classifier (the rule the attention kernels use to skip and
  * to take their unmasked fast path).  Rows [q0, q1) of the query tensor and
  * keys [k0, k1) of the key tensor, in the row numbering of bda_attn_fwd for

@@ -211,3 +211,28 @@ def multimodal_step(step: int, n: int, B: int = 2, Hq: int = 32, Hkv: int = 8, d
     vb = normal((B, Hkv, n, d), 1.0, g)
     logits, idx = planted_logits(B, n, V, sigma, g)
     return q, kb, vb, logits, idx
+
+
+def prefix_modality() -> torch.Tensor:
+    """Modality of the multimodal prefix positions (uint8 [PREFIX]): the image
+    span (merged image tokens and their row breaks) is 1, the text tail 0."""
+    m = torch.zeros(PREFIX, dtype=torch.uint8)
+    m[:IMAGE_TOKENS + ROW_BREAKS] = 1
+    return m
+
+
+def sprint_prefix(seed: int = 9, B: int = 2, Hkv: int = 8, d: int = 128, L: int = PREFIX,
+                  key_spread: float = 0.25):
+    """Prefix cache and per-position confidence for SPRINT pruning.
+
+    k, v [B, Hkv, L, d] bf16: N(0, 1) draws; each key row of position (b, i)
+    is scaled (in fp32, before the bf16 cast) by exp(key_spread * z_{b,i}),
+    z ~ N(0, 1) shared by the kv heads, so key norms vary across positions.
+    conf [B, L] fp32: U(0.05, 1).  Draw order: k, z, v, conf."""
+    g = _gen(seed)
+    k = torch.randn(B, Hkv, L, d, generator=g, dtype=torch.float32)
+    z = torch.randn(B, 1, L, 1, generator=g, dtype=torch.float32)
+    k = (k * torch.exp(key_spread * z)).to(torch.bfloat16)
+    v = normal((B, Hkv, L, d), 1.0, g)
+    conf = 0.05 + 0.95 * torch.rand(B, L, generator=g, dtype=torch.float32)
+    return k, v, conf

@@ -122,3 +122,52 @@ def test_row_stats_validation():
     assert need > 0
     assert f(A, 0, None, Bp, None, None, None, 1, 5, 10, Wp, need - 1, None) == 3
     assert f(A, 0, None, ctypes.c_void_p((1 << 32) + 16), None, None, None, 1, 5, 10, Wp, need, None) == 1  # overlap
+
+
+def test_sprint_validation():
+    f = bda.lib.bda_sprint_prune
+    E, Fp, Gp = (ctypes.c_void_p(x << 32) for x in (6, 7, 8))
+    need = bda.lib.bda_sprint_workspace_bytes(2, 64)
+    assert need >= 2 * 64 * 4 + 2 * 64          # norms and kept flags
+
+    # k, v, conf, modality, alpha, r_img, r_text, k_out, v_out, cap, kept, kept_count, scores,
+    # B, Hkv, L, d, ws, ws_bytes, stream
+    def call(**kw):
+        a = dict(k=A, v=Bp, conf=Cp, mod=Dp, alpha=0.5, r_img=0.8, r_text=1.0, ko=E, vo=Fp, cap=16,
+                 kept=Gp, kc=None, sc=None, B=2, H=8, L=64, d=128, ws=Wp, wsb=need)
+        a.update(kw)
+        return f(a["k"], a["v"], a["conf"], a["mod"], a["alpha"], a["r_img"], a["r_text"], a["ko"], a["vo"],
+                 a["cap"], a["kept"], a["kc"], a["sc"], a["B"], a["H"], a["L"], a["d"], a["ws"], a["wsb"], None)
+
+    assert call(d=96) == 2                       # head dim
+    assert call(L=16385) == 2                    # LDS-resident sort bound
+    assert call(B=0) == 1
+    assert call(alpha=1.5) == 1
+    assert call(r_img=-0.1) == 1
+    assert call(r_text=float("nan")) == 1
+    assert call(cap=-1) == 1
+    assert call(conf=None) == 1
+    assert call(kept=None) == 1
+    assert call(ko=None) == 1                    # gather requested without outputs
+    assert call(ws=None) == 3
+    assert call(wsb=need - 1) == 3
+    assert call(ko=ctypes.c_void_p((1 << 32) + 8)) == 1     # misaligned
+    assert call(ko=ctypes.c_void_p((1 << 32) + 4096)) == 1  # k_out inside k
+    assert call(kept=ctypes.c_void_p((2 << 32) + 64)) == 1  # kept inside v
+
+
+def test_sprint_kept_count():
+    kc = bda.lib.bda_sprint_kept_count
+    assert kc(3080, 1016, 0.8, 1.0) == 2464 + 1016
+    assert kc(5, 3, 0.5, 0.5) == 3 + 2             # floor(2.5 + 0.5), floor(1.5 + 0.5)
+    assert kc(0, 0, 0.8, 1.0) == 0
+    assert kc(-1, 0, 0.8, 1.0) == -1
+    assert kc(1, 1, 1.5, 1.0) == -1
+    # the oracle's count for the same modality mix
+    for n_img, n_txt, ri, rt in ((7, 3, 0.8, 1.0), (10, 10, 0.35, 0.65), (1, 0, 0.5, 0.5)):
+        L = n_img + n_txt
+        md = [1] * n_img + [0] * n_txt
+        k = [[[[1.0] * 4 for _ in range(L)]]]
+        conf = [[0.5] * L]
+        _, _, K = oracle.sprint(k, conf, md, 0.5, ri, rt)
+        assert kc(n_img, n_txt, ri, rt) == K
