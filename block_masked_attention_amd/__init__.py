@@ -26,7 +26,8 @@ _ENTRY_POINTS = (
     "bda_verify", "bda_verify_workspace_bytes", "bda_classify_tile", "bda_strerror",
     "bda_last_error", "bda_version", "bda_row_stats", "bda_row_stats_workspace_bytes",
     "bda_attn_fwd_lse", "bda_attn_bwd", "bda_attn_bwd_workspace_bytes", "bda_sprint_prune",
-    "bda_sprint_workspace_bytes", "bda_sprint_kept_count",
+    "bda_sprint_workspace_bytes", "bda_sprint_kept_count", "bda_attn_fwd_varlen", "bda_kv_append",
+    "bda_verify_crop",
 )
 
 
@@ -46,6 +47,12 @@ def _load():
     L.bda_attn_fwd.restype = I
     L.bda_attn_fwd_lse.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P, S, P]
     L.bda_attn_fwd_lse.restype = I
+    L.bda_attn_fwd_varlen.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P, S, P]
+    L.bda_attn_fwd_varlen.restype = I
+    L.bda_kv_append.argtypes = [P, P, P, P, P, I, I, I, I, I, P]
+    L.bda_kv_append.restype = I
+    L.bda_verify_crop.argtypes = [P, I, P, P, P, P, I, I, I, I, P, S, P]
+    L.bda_verify_crop.restype = I
     L.bda_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, S, P]
     L.bda_attn_bwd.restype = I
     L.bda_attn_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
@@ -208,6 +215,86 @@ def commit(logits, tokens, masked, threshold: float, k_min: int, workspace=None)
     if rc:
         raise BdaError(rc, "bda_commit")
     return tokens, masked
+
+
+def attn_fwd_varlen(q, k, v, kv_len, mode: str, block: int, out=None, workspace=None):
+    """DECODE/CAUSAL forward over a cache with per-row key counts: q
+    [B,Hq,n,d] with n = ``block``, k/v [B,Hkv,L_cap,d], ``kv_len`` int32 [B]
+    on the device (row b uses its first kv_len[b] keys, clamped to [n, L_cap];
+    its last n keys are the block)."""
+    m = MODE[mode]
+    if m == 0:
+        raise ValueError("per-row key counts apply to the decode and causal forms")
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or t.dim() != 4:
+            raise ValueError("q, k, v must be 4-D bfloat16")
+    dev = _check_dev(q, k, v, kv_len)
+    B, Hq, Sq, d = q.shape
+    Hkv, Lc = k.shape[1], k.shape[2]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d or Sq != block:
+        raise ValueError("shape mismatch")
+    if kv_len.dtype != torch.int32 or tuple(kv_len.shape) != (B,):
+        raise ValueError("kv_len must be int32 [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != torch.bfloat16:
+        raise ValueError("out must match q")
+    _check_dev(q, out)
+    need = attn_workspace_bytes(B, Hq, Hkv, Lc, d, block, m)
+    ws = _workspace(need, dev, workspace)
+    rc = lib.bda_attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(kv_len), B, Hq, Hkv, Lc, d, block, m,
+                                 _ptr(ws), need, _stream(dev))
+    if rc:
+        raise BdaError(rc, "bda_attn_fwd_varlen")
+    return out
+
+
+def kv_append(k_cache, v_cache, k_new, v_new, kv_len):
+    """Write the block rows k_new/v_new [B,Hkv,n,d] at rows kv_len[b]-n ..
+    kv_len[b]-1 of the caches [B,Hkv,L_cap,d] (in place)."""
+    for t in (k_cache, v_cache, k_new, v_new):
+        if t.dtype != torch.bfloat16 or t.dim() != 4:
+            raise ValueError("caches and new rows must be 4-D bfloat16")
+    if k_cache.shape != v_cache.shape or k_new.shape != v_new.shape:
+        raise ValueError("k and v shapes differ")
+    B, Hkv, Lc, d = k_cache.shape
+    n = k_new.shape[2]
+    if k_new.shape[0] != B or k_new.shape[1] != Hkv or k_new.shape[3] != d:
+        raise ValueError("new rows do not match the cache")
+    if kv_len.dtype != torch.int32 or tuple(kv_len.shape) != (B,):
+        raise ValueError("kv_len must be int32 [B]")
+    dev = _check_dev(k_cache, v_cache, k_new, v_new, kv_len)
+    rc = lib.bda_kv_append(_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(kv_len), B, Hkv, Lc, n, d,
+                           _stream(dev))
+    if rc:
+        raise BdaError(rc, "bda_kv_append")
+
+
+def verify_crop(logits, drafts, kv_len, kv_cap: int, argmax_out=None, accept_len=None, workspace=None):
+    """verify, then kv_len[b] = min(kv_len[b] + accept_len[b], kv_cap) on the
+    device.  Returns (argmax [B,R] int64, accept_len [B] int32)."""
+    if logits.dim() != 3:
+        raise ValueError("logits must be [B, R, V]")
+    B, R, V = logits.shape
+    dt = {torch.bfloat16: BF16, torch.float32: F32}.get(logits.dtype)
+    if dt is None:
+        raise ValueError("logits must be bfloat16 or float32")
+    if drafts.dtype != torch.int64 or tuple(drafts.shape) != (B, R):
+        raise ValueError("drafts must be int64 [B, R]")
+    if kv_len.dtype != torch.int32 or tuple(kv_len.shape) != (B,):
+        raise ValueError("kv_len must be int32 [B]")
+    dev = _check_dev(logits, drafts, kv_len, argmax_out, accept_len)
+    am = torch.empty(B, R, dtype=torch.int64, device=dev) if argmax_out is None else argmax_out
+    acc = torch.empty(B, dtype=torch.int32, device=dev) if accept_len is None else accept_len
+    if am.dtype != torch.int64 or tuple(am.shape) != (B, R) or acc.dtype != torch.int32 or tuple(acc.shape) != (B,):
+        raise ValueError("argmax_out must be int64 [B, R], accept_len int32 [B]")
+    need = int(lib.bda_verify_workspace_bytes(B, R, V))
+    ws = _workspace(need, dev, workspace)
+    rc = lib.bda_verify_crop(_ptr(logits), dt, _ptr(drafts), _ptr(am), _ptr(acc), _ptr(kv_len), kv_cap, B, R, V,
+                             _ptr(ws), need, _stream(dev))
+    if rc:
+        raise BdaError(rc, "bda_verify_crop")
+    return am, acc
 
 
 def verify(logits, drafts, workspace=None):

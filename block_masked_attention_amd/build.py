@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbda.so")
-SOURCES = ["attn.hip", "bwd.hip", "commit.hip", "sprint.hip", "api.cpp"]
+SOURCES = ["attn.hip", "bwd.hip", "cache.hip", "commit.hip", "sprint.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

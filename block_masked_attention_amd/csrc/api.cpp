@@ -72,9 +72,9 @@ size_t bda_attn_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int block,
   return p.ws_bytes;
 }
 
-static int attn_fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse, int B,
-                         int Hq, int Hkv, int L, int d, int block, int mode, void* workspace,
-                         size_t ws_bytes, void* stream) {
+static int attn_fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse,
+                         const int32_t* kv_len, int B, int Hq, int Hkv, int L, int d, int block, int mode,
+                         void* workspace, size_t ws_bytes, void* stream) {
   if (int e = check_attn(B, Hq, Hkv, L, d, block, mode)) return e;
   if (!q || !k || !v || !out) return fail(BDA_EINVAL, "q, k, v and out must be non-NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
@@ -89,6 +89,9 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, void* out,
   if (lse && (!aligned16(lse) || overlap(lse, lbytes, q, qbytes) || overlap(lse, lbytes, k, kbytes) ||
               overlap(lse, lbytes, v, kbytes) || overlap(lse, lbytes, out, qbytes)))
     return fail(BDA_EINVAL, "lse must be 16-byte aligned and must not overlap q, k, v or out");
+  if (kv_len && (((uintptr_t)kv_len & 3) || overlap(kv_len, (size_t)B * 4, out, qbytes) ||
+                 (lse && overlap(kv_len, (size_t)B * 4, lse, lbytes))))
+    return fail(BDA_EINVAL, "kv_len must be 4-byte aligned and must not overlap out or lse");
   bda::AttnPlan p;
   const char* why = "";
   if (int e = bda::attn_make_plan(B, Hq, Hkv, L, d, block, mode, &p, &why))
@@ -103,21 +106,34 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, void* out,
         (lse && overlap(workspace, p.ws_bytes, lse, lbytes)))
       return fail(BDA_EINVAL, "workspace overlaps a tensor argument");
   }
-  hipError_t e = bda::attn_launch(p, q, k, v, out, lse, workspace, (hipStream_t)stream);
+  if (kv_len && p.ws_bytes && overlap(workspace, p.ws_bytes, kv_len, (size_t)B * 4))
+    return fail(BDA_EINVAL, "workspace overlaps kv_len");
+  hipError_t e = bda::attn_launch(p, q, k, v, out, lse, kv_len, workspace, (hipStream_t)stream);
   if (e != hipSuccess) return fail(BDA_EHIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 
 int bda_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv,
                  int L, int d, int block, int mode, void* workspace, size_t ws_bytes, void* stream) {
-  return attn_fwd_impl(q, k, v, out, nullptr, B, Hq, Hkv, L, d, block, mode, workspace, ws_bytes, stream);
+  return attn_fwd_impl(q, k, v, out, nullptr, nullptr, B, Hq, Hkv, L, d, block, mode, workspace, ws_bytes,
+                       stream);
+}
+
+int bda_attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, const int32_t* kv_len, int B,
+                        int Hq, int Hkv, int L_cap, int d, int block, int mode, void* workspace,
+                        size_t ws_bytes, void* stream) {
+  if (mode != BDA_MODE_DECODE && mode != BDA_MODE_CAUSAL)
+    return fail(BDA_EUNSUPPORTED, "per-row key counts apply to the DECODE and CAUSAL forms only");
+  if (!kv_len) return fail(BDA_EINVAL, "kv_len must be non-NULL");
+  return attn_fwd_impl(q, k, v, out, nullptr, kv_len, B, Hq, Hkv, L_cap, d, block, mode, workspace, ws_bytes,
+                       stream);
 }
 
 int bda_attn_fwd_lse(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
                      int Hkv, int L, int d, int block, int mode, void* workspace, size_t ws_bytes,
                      void* stream) {
   if (!lse) return fail(BDA_EINVAL, "lse must be non-NULL");
-  return attn_fwd_impl(q, k, v, out, lse, B, Hq, Hkv, L, d, block, mode, workspace, ws_bytes, stream);
+  return attn_fwd_impl(q, k, v, out, lse, nullptr, B, Hq, Hkv, L, d, block, mode, workspace, ws_bytes, stream);
 }
 
 static int check_logits(const void* logits, int dtype, int G, int R, int V, const char* gname) {
@@ -165,9 +181,9 @@ int bda_commit(const void* logits, int dtype, int64_t* tokens, uint8_t* masked, 
 
 size_t bda_verify_workspace_bytes(int B, int R, int V) { return bda_commit_workspace_bytes(B, R, V); }
 
-int bda_verify(const void* logits, int dtype, const int64_t* drafts, int64_t* argmax_out,
-               int32_t* accept_len, int B, int R, int V, void* workspace, size_t ws_bytes,
-               void* stream) {
+static int verify_impl(const void* logits, int dtype, const int64_t* drafts, int64_t* argmax_out,
+                       int32_t* accept_len, int32_t* kv_len, int kv_cap, int B, int R, int V, void* workspace,
+                       size_t ws_bytes, void* stream) {
   if (int e = check_logits(logits, dtype, B, R, V, "B")) return e;
   if (B == 0) return ok();
   if (!accept_len) return fail(BDA_EINVAL, "accept_len must be non-NULL");
@@ -184,8 +200,47 @@ int bda_verify(const void* logits, int dtype, const int64_t* drafts, int64_t* ar
     return fail(BDA_EWORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_bytes,
                 workspace ? ws_bytes : (size_t)0);
   if (!aligned16(workspace)) return fail(BDA_EINVAL, "workspace must be 16-byte aligned");
-  hipError_t e = bda::verify_launch(p, logits, drafts, argmax_out, accept_len, workspace,
+  if (kv_len && (((uintptr_t)kv_len & 3) || overlap(kv_len, (size_t)B * 4, accept_len, (size_t)B * 4) ||
+                 overlap(kv_len, (size_t)B * 4, logits, lbytes) ||
+                 (rows && overlap(kv_len, (size_t)B * 4, argmax_out, rows * 8))))
+    return fail(BDA_EINVAL, "kv_len must be 4-byte aligned and must not overlap the other arguments");
+  hipError_t e = bda::verify_launch(p, logits, drafts, argmax_out, accept_len, kv_len, kv_cap, workspace,
                                     (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BDA_EHIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int bda_verify(const void* logits, int dtype, const int64_t* drafts, int64_t* argmax_out,
+               int32_t* accept_len, int B, int R, int V, void* workspace, size_t ws_bytes,
+               void* stream) {
+  return verify_impl(logits, dtype, drafts, argmax_out, accept_len, nullptr, 0, B, R, V, workspace, ws_bytes,
+                     stream);
+}
+
+int bda_verify_crop(const void* logits, int dtype, const int64_t* drafts, int64_t* argmax_out,
+                    int32_t* accept_len, int32_t* kv_len, int kv_cap, int B, int R, int V, void* workspace,
+                    size_t ws_bytes, void* stream) {
+  if (!kv_len) return fail(BDA_EINVAL, "kv_len must be non-NULL");
+  if (kv_cap < 1) return fail(BDA_EINVAL, "kv_cap must be >= 1");
+  return verify_impl(logits, dtype, drafts, argmax_out, accept_len, kv_len, kv_cap, B, R, V, workspace, ws_bytes,
+                     stream);
+}
+
+int bda_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new, const int32_t* kv_len,
+                  int B, int Hkv, int L_cap, int n, int d, void* stream) {
+  if (B < 0 || Hkv < 1 || n < 1 || L_cap < n) return fail(BDA_EINVAL, "need B >= 0, Hkv >= 1 and 1 <= n <= L_cap");
+  if (d != 32 && d != 64 && d != 128) return fail(BDA_EUNSUPPORTED, "d must be 32, 64 or 128");
+  if (B == 0) return ok();
+  if (!k_cache || !v_cache || !k_new || !v_new || !kv_len) return fail(BDA_EINVAL, "pointers must be non-NULL");
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new) || ((uintptr_t)kv_len & 3))
+    return fail(BDA_EINVAL, "caches and new rows must be 16-byte aligned, kv_len 4-byte aligned");
+  const size_t cb = (size_t)B * Hkv * L_cap * d * 2, nb = (size_t)B * Hkv * n * d * 2;
+  if (overlap(k_cache, cb, v_cache, cb) || overlap(k_cache, cb, k_new, nb) || overlap(k_cache, cb, v_new, nb) ||
+      overlap(v_cache, cb, k_new, nb) || overlap(v_cache, cb, v_new, nb) ||
+      overlap(k_cache, cb, kv_len, (size_t)B * 4) || overlap(v_cache, cb, kv_len, (size_t)B * 4))
+    return fail(BDA_EINVAL, "caches overlap each other or an input");
+  hipError_t e = bda::kv_append_launch(k_cache, v_cache, k_new, v_new, kv_len, B, Hkv, L_cap, n, d,
+                                       (hipStream_t)stream);
   if (e != hipSuccess) return fail(BDA_EHIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -36,6 +36,7 @@ struct AttnArgs {
   float* part_o;    // [split][B*Hq*n][D] unnormalised partial outputs
   float* part_ml;   // [split][B*Hq*n][2] (running max in log2 units, row sum)
   float* lse;       // optional [B*Hq*Sq]: natural-log log-sum-exp of each row's scores
+  const int32_t* kv_len;   // optional [B] (DECODE/CAUSAL): keys of each batch row, clamped to [n, L]
   int B, Hq, Hkv, G, mode, L, n, blk, Sq, Sk;
   int rows_per_wg, n_qtiles, n_splits, split_keys, pairs_per_xcd;
   int n_items;      // work items (batch x kv head x query tile x key split)
@@ -48,6 +49,7 @@ struct Geom {
   Span F, R1, R2;
   int nf, n1, nt;
   int pair, qt, split;
+  int L;            // keys of the item's batch row (DECODE/CAUSAL; HYBRID: L per half)
 };
 
 
@@ -100,6 +102,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       gm.qt = a.n_qtiles - 1 - rest / P;
     }
     Span F{0, 0}, R1{0, 0}, R2{0, 0};
+    gm.L = a.L;
     if (a.mode == kHybrid) {
       const int p0 = gm.qt * a.rows_per_wg;
       const int p1 = imin(a.L, p0 + a.rows_per_wg);
@@ -109,11 +112,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       R1 = Span{F.hi, a.L + e};                 // rest of the clean prefix / own clean blocks
       R2 = Span{s_min, e};                      // noisy blocks of these rows
     } else {
+      if (a.kv_len != nullptr) gm.L = imin(a.L, imax(a.n, a.kv_len[gm.pair / a.Hkv]));
+      const int Lb = gm.L;
       const int r0 = gm.qt * a.rows_per_wg;
       const int r1 = imin(a.n, r0 + a.rows_per_wg);
       const int lo = gm.split * a.split_keys;
-      const int hi = imin(a.mode == kDecode ? a.L : a.L - a.n + r1, lo + a.split_keys);
-      const int full_hi = imin(hi, a.mode == kDecode ? a.L : a.L - a.n + r0 + 1);
+      const int hi = imin(a.mode == kDecode ? Lb : Lb - a.n + r1, lo + a.split_keys);
+      const int full_hi = imin(hi, a.mode == kDecode ? Lb : Lb - a.n + r0 + 1);
       const int nfull = full_hi > lo ? (full_hi - lo) / kBN : 0;
       F = Span{lo, lo + nfull * kBN};
       R1 = Span{F.hi, imax(F.hi, hi)};
@@ -434,7 +439,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
     for (int qb = 0; qb < NQB; ++qb) {
       A[qb] = Span{0, 0};
       C[qb] = Span{0, 0};
-      if (valid[qb]) row_spans(a.mode, a.L, a.n, a.blk, qrow[qb], A[qb], C[qb]);
+      if (valid[qb]) row_spans(a.mode, cur.L, a.n, a.blk, qrow[qb], A[qb], C[qb]);
     }
 #pragma unroll 1
     for (int sub = 0; sub < 2; ++sub) {
@@ -783,9 +788,10 @@ static hipError_t launch_d(const AttnPlan& p, AttnArgs a, hipStream_t st) {
 }
 
 hipError_t attn_launch(const AttnPlan& p, const void* q, const void* k, const void* v, void* out,
-                       float* lse, void* ws, hipStream_t st) {
+                       float* lse, const int32_t* kv_len, void* ws, hipStream_t st) {
   AttnArgs a{};
   a.lse = lse;
+  a.kv_len = kv_len;
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k;
   a.v = (const uint16_t*)v;

@@ -323,7 +323,8 @@ __global__ __launch_bounds__(kCommitThreads) void commit_finalize_kernel(
 // One workgroup per sequence: argmax per row, then the first disagreement.
 __global__ __launch_bounds__(kCommitThreads) void verify_finalize_kernel(
     const Partial* __restrict__ part, int n_chunks, const int64_t* __restrict__ drafts,
-    int64_t* __restrict__ argmax_out, int32_t* __restrict__ accept, int R) {
+    int64_t* __restrict__ argmax_out, int32_t* __restrict__ accept, int R, int32_t* __restrict__ kv_len,
+    int kv_cap) {
   __shared__ int red[kCommitThreads / 64];
   const int b = blockIdx.x;
   int first = R;
@@ -341,6 +342,7 @@ __global__ __launch_bounds__(kCommitThreads) void verify_finalize_kernel(
     int m = red[0];
     for (int w = 1; w < kCommitThreads / 64; ++w) m = min(m, red[w]);
     accept[b] = m;
+    if (kv_len != nullptr) kv_len[b] = min(kv_len[b] + m, kv_cap);   // keep the accepted drafts' rows
   }
 }
 
@@ -451,7 +453,8 @@ hipError_t commit_launch(const CommitPlan& p, const void* logits, int64_t* token
 }
 
 hipError_t verify_launch(const CommitPlan& p, const void* logits, const int64_t* drafts,
-                         int64_t* argmax_out, int32_t* accept, void* ws, hipStream_t st) {
+                         int64_t* argmax_out, int32_t* accept, int32_t* kv_len, int kv_cap, void* ws,
+                         hipStream_t st) {
   if (p.G == 0) return hipSuccess;
   Partial* part;
   float* rowp;
@@ -464,7 +467,7 @@ hipError_t verify_launch(const CommitPlan& p, const void* logits, const int64_t*
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(verify_finalize_kernel, dim3(p.G), dim3(kCommitThreads), 0, st, part,
-                     p.n_chunks, drafts, argmax_out, accept, p.R);
+                     p.n_chunks, drafts, argmax_out, accept, p.R, kv_len, kv_cap);
   return hipGetLastError();
 }
 

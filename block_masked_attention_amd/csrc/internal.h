@@ -27,7 +27,7 @@ struct AttnPlan {
 int attn_make_plan(int B, int Hq, int Hkv, int L, int d, int block, int mode, AttnPlan* p,
                    const char** why);
 hipError_t attn_launch(const AttnPlan& p, const void* q, const void* k, const void* v, void* out,
-                       float* lse, void* ws, hipStream_t st);
+                       float* lse, const int32_t* kv_len, void* ws, hipStream_t st);
 
 struct CommitPlan {
   int G, R, V, dtype;
@@ -43,7 +43,10 @@ hipError_t stats_launch(const CommitPlan& p, const void* logits, const uint8_t* 
                         int64_t* argmax_out, float* entropy, float* mean_entropy, void* ws,
                         hipStream_t st);
 hipError_t verify_launch(const CommitPlan& p, const void* logits, const int64_t* drafts,
-                         int64_t* argmax_out, int32_t* accept, void* ws, hipStream_t st);
+                         int64_t* argmax_out, int32_t* accept, int32_t* kv_len, int kv_cap, void* ws,
+                         hipStream_t st);
+hipError_t kv_append_launch(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                            const int32_t* kv_len, int B, int Hkv, int L_cap, int n, int d, hipStream_t st);
 
 // Backward of the training form (hybrid mask).
 struct BwdPlan {

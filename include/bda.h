@@ -96,6 +96,34 @@ int bda_attn_fwd_lse(const void* q, const void* k, const void* v, void* out, flo
                      void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * DECODE / CAUSAL forward over a cache whose rows hold different numbers of
+ * keys: the draft and validation passes of linear speculative decoding
+ * ([NLD-3x] sec. 2, "generate and validate") once sequences have accepted
+ * different numbers of drafts (its KV-cache strategy crops each cache to
+ * what was kept).  k, v are [B, Hkv, L_cap, d] (the capacity is the row
+ * stride); kv_len [B] (int32, device, read by the kernels) gives the keys of
+ * each batch row, L_b = kv_len[b] clamped to [block, L_cap]; its last `block`
+ * keys are the active block.  Row b then behaves exactly as bda_attn_fwd with
+ * L = L_b; keys past L_b are never read.  mode must be BDA_MODE_DECODE or
+ * BDA_MODE_CAUSAL (else BDA_EUNSUPPORTED).  Workspace as bda_attn_fwd with
+ * L = L_cap.  The lengths stay on the device, so a captured graph can replay
+ * the call as they change.
+ */
+int bda_attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, const int32_t* kv_len,
+                        int B, int Hq, int Hkv, int L_cap, int d, int block, int mode,
+                        void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Writes a block's fresh K/V rows into a cache with per-row lengths (the KV
+ * update of [NLD-3x] sec. 2): k_cache[b, h, L_b - n + j] = k_new[b, h, j]
+ * for j < n, same for v, with L_b = kv_len[b] clamped to [n, L_cap] as in
+ * bda_attn_fwd_varlen.  k_cache, v_cache [B, Hkv, L_cap, d] bf16; k_new,
+ * v_new [B, Hkv, n, d] bf16; kv_len [B] int32 (device).  d in {32, 64, 128}.
+ */
+int bda_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new, const int32_t* kv_len,
+                  int B, int Hkv, int L_cap, int n, int d, void* stream);
+
+/*
  * Backward of the training form (mode must be BDA_MODE_HYBRID; others return
  * BDA_EUNSUPPORTED) ([NLD-3x] sec. 1 mask; the [LLaDA] BDLM objective trains
  * through it).  For loss = sum(dout * out) with out = bda_attn_fwd(q, k, v):
@@ -146,6 +174,19 @@ int bda_verify(const void* logits, int dtype, const int64_t* drafts,
                int64_t* argmax_out, int32_t* accept_len, int B, int R, int V,
                void* workspace, size_t ws_bytes, void* stream);
 size_t bda_verify_workspace_bytes(int B, int R, int V);
+
+/*
+ * bda_verify, then the crop of [NLD-3x]'s KV-cache strategy on the device:
+ * kv_len[b] = min(kv_len[b] + accept_len[b], kv_cap) (int32, device,
+ * read and written).  With kv_len counting the cached keys plus the block of
+ * R drafts (as bda_attn_fwd_varlen takes it), the result counts the kept
+ * prefix, now including the accepted drafts, plus room for the next block of
+ * R rows; rows of rejected drafts are overwritten by the next bda_kv_append.
+ * Same workspace as bda_verify.
+ */
+int bda_verify_crop(const void* logits, int dtype, const int64_t* drafts, int64_t* argmax_out,
+                    int32_t* accept_len, int32_t* kv_len, int kv_cap, int B, int R, int V,
+                    void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * Per-row statistics of a softmax over the vocabulary, for adaptive stopping

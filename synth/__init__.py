@@ -40,17 +40,21 @@ def normal(shape, sigma: float, g: torch.Generator, dtype=torch.bfloat16) -> tor
 
 
 def planted_logits(G: int, R: int, V: int, sigma: float, g: torch.Generator,
-                   dtype=torch.bfloat16, lo: float = 2.0, hi: float = 12.0):
+                   dtype=torch.bfloat16, lo: float = 2.0, hi: float = 12.0, idx=None):
     """Noise logits with one planted peak per row.
 
     Each row is N(0, sigma^2) noise (cast to ``dtype``); a uniformly drawn
-    index is then overwritten with (largest noise value of that row) + U(lo, hi),
-    cast to ``dtype``.  The planted index is returned: it is the row's unique
-    largest entry by construction (the gap is at least ``lo`` before rounding).
-    Draw order: noise, planted indices, offsets.
+    index (or the given ``idx`` [G, R]) is then overwritten with (largest
+    noise value of that row) + U(lo, hi), cast to ``dtype``.  The planted index
+    is returned: it is the row's unique largest entry by construction (the gap
+    is at least ``lo`` before rounding).  Draw order: noise, planted indices
+    (when not given), offsets.
     """
     noise = normal((G, R, V), sigma, g, dtype)
-    idx = torch.randint(0, V, (G, R), generator=g, dtype=torch.int64)
+    if idx is None:
+        idx = torch.randint(0, V, (G, R), generator=g, dtype=torch.int64)
+    else:
+        idx = idx.to(torch.int64).clone()
     off = lo + (hi - lo) * torch.rand(G, R, generator=g, dtype=torch.float32)
     top = noise.float().amax(dim=-1)
     peak = (top + off).to(dtype)
@@ -236,3 +240,59 @@ def sprint_prefix(seed: int = 9, B: int = 2, Hkv: int = 8, d: int = 128, L: int 
     v = normal((B, Hkv, L, d), 1.0, g)
     conf = 0.05 + 0.95 * torch.rand(B, L, generator=g, dtype=torch.float32)
     return k, v, conf
+
+
+# --------------------------------------------------------------------------
+# Linear speculative loop with per-sequence cache lengths
+# --------------------------------------------------------------------------
+
+def spec_prefix(seed: int = 20, prefix=(517, 1000, 2345, 3000), cap: int = 3328, n: int = 28,
+                Hkv: int = 8, d: int = 128):
+    """Cache [B, Hkv, cap, d] bf16 N(0, 1) (rows past each prefix are filled
+    too, so a read past a sequence's length would show) and the starting
+    per-sequence key counts kv_len = prefix + n (int32)."""
+    g = _gen(seed)
+    B = len(prefix)
+    k = normal((B, Hkv, cap, d), 1.0, g)
+    v = normal((B, Hkv, cap, d), 1.0, g)
+    kv_len = torch.tensor([p + n for p in prefix], dtype=torch.int32)
+    return k, v, kv_len
+
+
+def spec_step(step: int, B: int = 4, n: int = 28, Hq: int = 32, Hkv: int = 8, d: int = 128,
+              V: int = 32768, sigma: float = 3.0, p: float = 0.25):
+    """Inputs of speculative step ``step`` (seed 200 + step), in draw order:
+    draft queries and block K/V rows, draft logits [B, n, V] with planted
+    peaks (the drafts are their argmax), verify queries and block K/V rows,
+    accept lengths a_b ~ Geometric(p) - 1 capped at n, and verify logits
+    planted at the drafts for j < a_b, at a different id for j = a_b and at
+    uniform ids after."""
+    g = _gen(200 + step)
+    qd = normal((B, Hq, n, d), 1.0, g)
+    kd = normal((B, Hkv, n, d), 1.0, g)
+    vd = normal((B, Hkv, n, d), 1.0, g)
+    dlog, drafts = planted_logits(B, n, V, sigma, g)
+    qv = normal((B, Hq, n, d), 1.0, g)
+    kv = normal((B, Hkv, n, d), 1.0, g)
+    vv = normal((B, Hkv, n, d), 1.0, g)
+    u = torch.rand(B, generator=g, dtype=torch.float64)
+    acc = torch.floor(torch.log1p(-u) / math.log1p(-p)).to(torch.int64).clamp(max=n)
+    r = torch.randint(0, V - 1, (B,), generator=g, dtype=torch.int64)
+    vidx = torch.randint(0, V, (B, n), generator=g, dtype=torch.int64)
+    for b in range(B):
+        a = int(acc[b])
+        vidx[b, :a] = drafts[b, :a]
+        if a < n:
+            vidx[b, a] = (drafts[b, a] + 1 + r[b]) % V
+    vlog, _ = planted_logits(B, n, V, sigma, g, idx=vidx)
+    return dict(qd=qd, kd=kd, vd=vd, dlog=dlog, drafts=drafts, qv=qv, kv=kv, vv=vv, vlog=vlog, accept=acc)
+
+
+def varlen_case(seed: int, B: int, Hq: int, Hkv: int, d: int, n: int, cap: int):
+    """q [B, Hq, n, d] and a cache k, v [B, Hkv, cap, d], bf16 N(0, 1), drawn
+    in that order."""
+    g = _gen(seed)
+    q = normal((B, Hq, n, d), 1.0, g)
+    k = normal((B, Hkv, cap, d), 1.0, g)
+    v = normal((B, Hkv, cap, d), 1.0, g)
+    return q, k, v

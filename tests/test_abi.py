@@ -171,3 +171,28 @@ def test_sprint_kept_count():
         conf = [[0.5] * L]
         _, _, K = oracle.sprint(k, conf, md, 0.5, ri, rt)
         assert kc(n_img, n_txt, ri, rt) == K
+
+
+def test_varlen_cache_validation():
+    f = bda.lib.bda_attn_fwd_varlen
+    E = ctypes.c_void_p(6 << 32)
+    # q, k, v, out, kv_len, B, Hq, Hkv, L_cap, d, block, mode, ws, ws_bytes, stream
+    assert f(A, Bp, Cp, Dp, E, 2, 32, 8, 256, 128, 28, 0, None, 0, None) == 2        # hybrid
+    assert f(A, Bp, Cp, Dp, None, 2, 32, 8, 256, 128, 28, 1, None, 0, None) == 1     # no lengths
+    assert f(A, Bp, Cp, Dp, ctypes.c_void_p((6 << 32) + 2), 2, 32, 8, 256, 128, 28, 1, None, 0, None) == 1
+    assert f(A, Bp, Cp, Dp, ctypes.c_void_p((4 << 32) + 16), 2, 32, 8, 256, 128, 28, 2, None, 0, None) == 1  # in out
+    assert f(A, Bp, Cp, Dp, E, 2, 32, 8, 20, 128, 28, 1, None, 0, None) == 1          # block > capacity
+    a = bda.lib.bda_kv_append
+    # k_cache, v_cache, k_new, v_new, kv_len, B, Hkv, L_cap, n, d, stream
+    assert a(A, Bp, Cp, Dp, E, 0, 8, 256, 28, 128, None) == 0                          # nothing to do
+    assert a(A, Bp, Cp, Dp, E, 2, 8, 256, 28, 96, None) == 2
+    assert a(A, Bp, Cp, Dp, E, 2, 8, 20, 28, 128, None) == 1
+    assert a(A, Bp, None, Dp, E, 2, 8, 256, 28, 128, None) == 1
+    assert a(A, ctypes.c_void_p((1 << 32) + 4096), Cp, Dp, E, 2, 8, 256, 28, 128, None) == 1   # caches overlap
+    assert a(A, Bp, Cp, Dp, ctypes.c_void_p((1 << 32) + 64), 2, 8, 256, 28, 128, None) == 1    # lengths in a cache
+    c = bda.lib.bda_verify_crop
+    # logits, dtype, drafts, argmax, accept, kv_len, kv_cap, B, R, V, ws, ws_bytes, stream
+    assert c(A, 0, Bp, Cp, Dp, None, 100, 2, 28, 100, Wp, 1 << 20, None) == 1
+    assert c(A, 0, Bp, Cp, Dp, E, 0, 2, 28, 100, Wp, 1 << 20, None) == 1
+    assert c(A, 0, Bp, Cp, Dp, ctypes.c_void_p((4 << 32) + 4), 100, 2, 28, 100, Wp, 1 << 20, None) == 1  # in accept
+    assert c(A, 0, Bp, Cp, Dp, E, 100, 2, 28, 100, None, 0, None) == 3
