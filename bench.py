@@ -388,6 +388,16 @@ def secondary(bda, synth, torch, dev, args):
     del pk, pv, pconf, pmod, ko, vo, spws
     torch.cuda.empty_cache()
 
+    # ---- one linear speculative step on the device, eager launches vs one
+    # HIP graph replay: append the draft rows, DECODE attention, drafts =
+    # argmax of the draft logits, append the validation rows, CAUSAL
+    # attention, verify + crop.  16 sequences of ~8k cached keys, 28 drafts,
+    # vocabulary 131072 (the verify workload's shapes); the lengths are reset
+    # before each timed call.
+    res["speculative_step"] = speculative_step(bda, synth, torch, dev, iters)
+    log(f"[bench] speculative_step: {res['speculative_step']}")
+    torch.cuda.empty_cache()
+
     # ---- verify on [16, 28, 131072] bf16
     vl, vidx, _ = synth.commit_logits(seed=6, G=16, R=28)
     drafts, _ = synth.verify_drafts(vidx)
@@ -401,6 +411,57 @@ def secondary(bda, synth, torch, dev, args):
                      "algorithmic_bytes": byts}
     log(f"[bench] verify: {res['verify']}")
     return res
+
+
+def speculative_step(bda, synth, torch, dev, iters):
+    B, Hq, Hkv, d, n, V = 16, 32, 8, 128, 28, synth.VOCAB
+    prefix = tuple(8192 - 37 * b for b in range(B))
+    cap = 8192 + n + 8 * n
+    k0, v0, kl0 = synth.spec_prefix(seed=21, prefix=prefix, cap=cap, n=n, Hkv=Hkv, d=d)
+    s = synth.spec_step(0, B=B, n=n, Hq=Hq, Hkv=Hkv, d=d, V=V)
+    kc, vc, kl, kl_init = k0.to(dev), v0.to(dev), kl0.to(dev), kl0.to(dev)
+    x = {key: s[key].to(dev) for key in ("qd", "kd", "vd", "dlog", "qv", "kv", "vv", "vlog")}
+    od, ov = torch.empty_like(x["qd"]), torch.empty_like(x["qd"])
+    drafts = torch.empty(B, n, dtype=torch.int64, device=dev)
+    am = torch.empty(B, n, dtype=torch.int64, device=dev)
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    u8 = torch.uint8
+    ws_d = torch.empty(max(1, bda.attn_workspace_bytes(B, Hq, Hkv, cap, d, n, "decode")), dtype=u8, device=dev)
+    ws_v = torch.empty(max(1, bda.attn_workspace_bytes(B, Hq, Hkv, cap, d, n, "causal")), dtype=u8, device=dev)
+    n_s = int(bda.lib.bda_row_stats_workspace_bytes(B, n, V))
+    ws_s = torch.empty(n_s, dtype=u8, device=dev)
+    ws_c = torch.empty(int(bda.lib.bda_verify_workspace_bytes(B, n, V)), dtype=u8, device=dev)
+
+    def step():
+        bda.kv_append(kc, vc, x["kd"], x["vd"], kl)
+        bda.attn_fwd_varlen(x["qd"], kc, vc, kl, "decode", n, out=od, workspace=ws_d)
+        rc = bda.lib.bda_row_stats(bda._ptr(x["dlog"]), bda.BF16, None, None, bda._ptr(drafts), None, None, B, n, V,
+                                   bda._ptr(ws_s), n_s, bda._stream(dev))
+        if rc:
+            raise RuntimeError("bda_row_stats failed")
+        bda.kv_append(kc, vc, x["kv"], x["vv"], kl)
+        bda.attn_fwd_varlen(x["qv"], kc, vc, kl, "causal", n, out=ov, workspace=ws_v)
+        bda.verify_crop(x["vlog"], drafts, kl, cap, argmax_out=am, accept_len=acc, workspace=ws_c)
+
+    def reset(i):
+        kl.copy_(kl_init)
+
+    step()
+    torch.cuda.synchronize()
+    accepted = int(acc.sum().item())
+    t_eager, _ = time_launches(lambda i: step(), iters, 5, pre=reset)
+    graph = torch.cuda.CUDAGraph()
+    reset(0)
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    t_graph, _ = time_launches(lambda i: graph.replay(), iters, 5, pre=reset)
+    keys = sum(prefix) + B * n
+    byts = 2 * (keys * Hkv * d * 2 * 2) + 2 * B * n * V * 2 + 4 * B * n * Hq * d * 2
+    return {"B": B, "drafts": n, "kv_len": [min(prefix) + n, max(prefix) + n], "V": V,
+            "us_per_step_eager": round(t_eager * 1e3, 2), "us_per_step_graph": round(t_graph * 1e3, 2),
+            "hbm_floor_us": round(byts / PEAK_HBM_GBS / 1e3, 2), "accepted_per_step": accepted,
+            "accepted_tokens_per_s_graph": round(accepted / (t_graph * 1e-3), 1)}
 
 
 if __name__ == "__main__":

@@ -36,11 +36,11 @@ struct AttnArgs {
   float* part_o;    // [split][B*Hq*n][D] unnormalised partial outputs
   float* part_ml;   // [split][B*Hq*n][2] (running max in log2 units, row sum)
   float* lse;       // optional [B*Hq*Sq]: natural-log log-sum-exp of each row's scores
-  const int32_t* kv_len;   // optional [B] (DECODE/CAUSAL): keys of each batch row, clamped to [n, L]
   int B, Hq, Hkv, G, mode, L, n, blk, Sq, Sk;
   int rows_per_wg, n_qtiles, n_splits, split_keys, pairs_per_xcd;
   int n_items;      // work items (batch x kv head x query tile x key split)
   float sl2;        // log2(e) / sqrt(D)
+  const int32_t* kv_len;   // optional [B] (DECODE/CAUSAL): keys of each batch row, clamped to [n, L]
 };
 
 // Geometry of one work item: its (batch, kv head) pair, query tile and key
@@ -61,7 +61,7 @@ struct Geom {
 // STAGES = 2: a register-staged double-buffered walk whose smaller LDS
 // footprint lets two 4-wave workgroups share a CU, for short query blocks
 // over long caches (decode, verify).
-template <int D, int NW, int QPW, int STAGES>
+template <int D, int NW, int QPW, int STAGES, bool VARLEN>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) {
   constexpr int NQB = QPW / 32;               // 32-query column blocks per wavefront
   constexpr int NT = NW * 64;
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       gm.qt = a.n_qtiles - 1 - rest / P;
     }
     Span F{0, 0}, R1{0, 0}, R2{0, 0};
-    gm.L = a.L;
+    if constexpr (VARLEN) gm.L = a.L;
     if (a.mode == kHybrid) {
       const int p0 = gm.qt * a.rows_per_wg;
       const int p1 = imin(a.L, p0 + a.rows_per_wg);
@@ -112,8 +112,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       R1 = Span{F.hi, a.L + e};                 // rest of the clean prefix / own clean blocks
       R2 = Span{s_min, e};                      // noisy blocks of these rows
     } else {
-      if (a.kv_len != nullptr) gm.L = imin(a.L, imax(a.n, a.kv_len[gm.pair / a.Hkv]));
-      const int Lb = gm.L;
+      int Lb = a.L;
+      if constexpr (VARLEN) {
+        Lb = imin(a.L, imax(a.n, a.kv_len[gm.pair / a.Hkv]));
+        gm.L = Lb;
+      }
       const int r0 = gm.qt * a.rows_per_wg;
       const int r1 = imin(a.n, r0 + a.rows_per_wg);
       const int lo = gm.split * a.split_keys;
@@ -439,7 +442,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
     for (int qb = 0; qb < NQB; ++qb) {
       A[qb] = Span{0, 0};
       C[qb] = Span{0, 0};
-      if (valid[qb]) row_spans(a.mode, cur.L, a.n, a.blk, qrow[qb], A[qb], C[qb]);
+      if (valid[qb]) row_spans(a.mode, VARLEN ? cur.L : a.L, a.n, a.blk, qrow[qb], A[qb], C[qb]);
     }
 #pragma unroll 1
     for (int sub = 0; sub < 2; ++sub) {
@@ -748,7 +751,10 @@ int attn_make_plan(int B, int Hq, int Hkv, int L, int d, int block, int mode, At
 
 template <int D, int NW, int QPW, int STAGES>
 static hipError_t launch_main(const AttnArgs& a, long long grid, hipStream_t st) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, QPW, STAGES>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a);
+  if (a.kv_len != nullptr)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, NW, QPW, STAGES, true>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<D, NW, QPW, STAGES, false>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a);
   return hipGetLastError();
 }
 
