@@ -217,7 +217,7 @@ def main():
 def _kernel_sha():
     import hashlib
     h = hashlib.sha256()
-    for f in ("attn.hip", "common.h", "geometry.h"):
+    for f in ("attn.hip", "common.h", "geometry.h", "tiles.h"):
         with open(os.path.join(ROOT, "block_masked_attention_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

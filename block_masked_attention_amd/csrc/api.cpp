@@ -89,6 +89,7 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, void* out,
   if (lse && (!aligned16(lse) || overlap(lse, lbytes, q, qbytes) || overlap(lse, lbytes, k, kbytes) ||
               overlap(lse, lbytes, v, kbytes) || overlap(lse, lbytes, out, qbytes)))
     return fail(BDA_EINVAL, "lse must be 16-byte aligned and must not overlap q, k, v or out");
+  if (kv_len && lse) return fail(BDA_EUNSUPPORTED, "per-row key counts with the log-sum-exp output");
   if (kv_len && (((uintptr_t)kv_len & 3) || overlap(kv_len, (size_t)B * 4, out, qbytes) ||
                  (lse && overlap(kv_len, (size_t)B * 4, lse, lbytes))))
     return fail(BDA_EINVAL, "kv_len must be 4-byte aligned and must not overlap out or lse");

@@ -35,12 +35,12 @@ struct AttnArgs {
   uint16_t* out;
   float* part_o;    // [split][B*Hq*n][D] unnormalised partial outputs
   float* part_ml;   // [split][B*Hq*n][2] (running max in log2 units, row sum)
-  float* lse;       // optional [B*Hq*Sq]: natural-log log-sum-exp of each row's scores
   int B, Hq, Hkv, G, mode, L, n, blk, Sq, Sk;
   int rows_per_wg, n_qtiles, n_splits, split_keys, pairs_per_xcd;
   int n_items;      // work items (batch x kv head x query tile x key split)
   float sl2;        // log2(e) / sqrt(D)
   const int32_t* kv_len;   // optional [B] (DECODE/CAUSAL): keys of each batch row, clamped to [n, L]
+  float* lse;       // optional [B*Hq*Sq]: natural-log log-sum-exp of each row's scores
 };
 
 // Geometry of one work item: its (batch, kv head) pair, query tile and key
@@ -61,7 +61,7 @@ struct Geom {
 // STAGES = 2: a register-staged double-buffered walk whose smaller LDS
 // footprint lets two 4-wave workgroups share a CU, for short query blocks
 // over long caches (decode, verify).
-template <int D, int NW, int QPW, int STAGES, bool VARLEN>
+template <int D, int NW, int QPW, int STAGES, bool VARLEN, bool LSE>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) {
   constexpr int NQB = QPW / 32;               // 32-query column blocks per wavefront
   constexpr int NT = NW * 64;
@@ -486,7 +486,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       if (!valid[qb]) continue;
       if (a.n_splits == 1) {
         const float inv = 1.f / l_tot;
-        if (a.lse != nullptr && hb == 0)
+        if (LSE && hb == 0)
           a.lse[(size_t)(b * a.Hq + head[qb]) * a.Sq + qrow[qb]] = (m_run[qb] * sl2 + __log2f(l_tot)) * 0.6931471805599453f;
         uint16_t* op = a.out + ((size_t)(b * a.Hq + head[qb]) * a.Sq + qrow[qb]) * D + 4 * hb;
 #pragma unroll
@@ -751,10 +751,17 @@ int attn_make_plan(int B, int Hq, int Hkv, int L, int d, int block, int mode, At
 
 template <int D, int NW, int QPW, int STAGES>
 static hipError_t launch_main(const AttnArgs& a, long long grid, hipStream_t st) {
+  // per-row key counts and the log-sum-exp output are compiled in only where
+  // asked for (the API never asks for both at once)
   if (a.kv_len != nullptr)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, NW, QPW, STAGES, true>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, NW, QPW, STAGES, true, false>), dim3((unsigned)grid), dim3(NW * 64), 0,
+                       st, a);
+  else if (a.lse != nullptr)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, NW, QPW, STAGES, false, true>), dim3((unsigned)grid), dim3(NW * 64), 0,
+                       st, a);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, NW, QPW, STAGES, false>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, NW, QPW, STAGES, false, false>), dim3((unsigned)grid), dim3(NW * 64), 0,
+                       st, a);
   return hipGetLastError();
 }
 
