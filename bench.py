@@ -54,16 +54,44 @@ def causal_pairs(L, n):
     return n * (L - n) + n * (n + 1) // 2
 
 
-def time_launches(fn, iters, warmup, pre=None):
-    """Mean and median per-launch ms of fn(i) with HIP events on the current stream."""
+_SLEEP_CYCLES_PER_MS = None
+
+
+def _sleep_cycles_per_ms():
+    """GPU spin cycles per millisecond of torch.cuda._sleep, measured once."""
+    global _SLEEP_CYCLES_PER_MS
+    if _SLEEP_CYCLES_PER_MS is None:
+        import torch
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        a.record()
+        torch.cuda._sleep(1_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_MS = 1_000_000 / max(a.elapsed_time(b), 1e-3)
+    return _SLEEP_CYCLES_PER_MS
+
+
+def time_launches(fn, iters, warmup, pre=None, queue=True):
+    """Mean and median per-launch ms of fn(i) with HIP events on the current
+    stream.  The timed launches are queued behind a GPU sleep long enough for
+    the host to enqueue all of them, so each event pair measures the GPU's
+    back-to-back time for the call and not the host's launch overhead (the
+    ctypes call and argument checks take tens of microseconds, as long as a
+    small kernel).  queue=False times each call as the host issues it."""
+    import time
     import torch
+    t0 = time.perf_counter()
     for i in range(warmup):
         if pre:
             pre(i)
         fn(i)
     torch.cuda.synchronize()
+    host_ms = (time.perf_counter() - t0) * 1e3 / max(warmup, 1)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    if queue:
+        torch.cuda._sleep(int(_sleep_cycles_per_ms() * min(2.0 * host_ms * iters + 1.0, 200.0)))
     for i in range(iters):
         if pre:
             pre(i)
@@ -450,16 +478,20 @@ def speculative_step(bda, synth, torch, dev, iters):
     torch.cuda.synchronize()
     accepted = int(acc.sum().item())
     t_eager, _ = time_launches(lambda i: step(), iters, 5, pre=reset)
+    t_eager_host, _ = time_launches(lambda i: step(), iters, 5, pre=reset, queue=False)
     graph = torch.cuda.CUDAGraph()
     reset(0)
     with torch.cuda.graph(graph):
         step()
     torch.cuda.synchronize()
     t_graph, _ = time_launches(lambda i: graph.replay(), iters, 5, pre=reset)
+    t_graph_host, _ = time_launches(lambda i: graph.replay(), iters, 5, pre=reset, queue=False)
     keys = sum(prefix) + B * n
     byts = 2 * (keys * Hkv * d * 2 * 2) + 2 * B * n * V * 2 + 4 * B * n * Hq * d * 2
     return {"B": B, "drafts": n, "kv_len": [min(prefix) + n, max(prefix) + n], "V": V,
             "us_per_step_eager": round(t_eager * 1e3, 2), "us_per_step_graph": round(t_graph * 1e3, 2),
+            "us_per_step_eager_as_issued": round(t_eager_host * 1e3, 2),
+            "us_per_step_graph_as_issued": round(t_graph_host * 1e3, 2),
             "hbm_floor_us": round(byts / PEAK_HBM_GBS / 1e3, 2), "accepted_per_step": accepted,
             "accepted_tokens_per_s_graph": round(accepted / (t_graph * 1e-3), 1)}
 
