@@ -647,7 +647,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
 }
 
 // Fixed-order log-sum-exp merge of the key splits of DECODE/CAUSAL calls.
-template <int D>
+template <int D, int SB>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
                                                            uint16_t* __restrict__ out, float* __restrict__ lse,
@@ -657,17 +657,40 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   const long long row = t / TPR;
   const int c = (int)(t - row * TPR) * 4;
   if (row >= rows) return;
-  float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, part_ml[((size_t)s * rows + row) * 2]);
-  float l = 0.f;
+  // Splits in batches of SB (the host picks the smallest power of two that
+  // covers the splits, at most 32) whose loads all go out before any
+  // arithmetic; within a batch the weights are taken against the batch's
+  // maximum, and the running sums are rescaled when a batch raises it.
+  // Split 0 always holds keys, so M is finite after the first batch.
+  float M = -INFINITY, l = 0.f;
   f32x4 acc{0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < n_splits; ++s) {
-    const float ms = part_ml[((size_t)s * rows + row) * 2];
-    if (ms == -INFINITY) continue;
-    const float wgt = exp2_fast(ms - M);
-    l += wgt * part_ml[((size_t)s * rows + row) * 2 + 1];
-    const f32x4 x = *(const f32x4*)(part_o + ((size_t)s * rows + row) * D + c);
-    acc += wgt * x;
+  for (int s0 = 0; s0 < n_splits; s0 += SB) {
+    f32x2 ml[SB];
+    f32x4 x[SB];
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      const size_t sr = (size_t)imin(s0 + j, n_splits - 1) * rows + row;
+      ml[j] = *(const f32x2*)(part_ml + sr * 2);
+      x[j] = *(const f32x4*)(part_o + sr * D + c);
+    }
+    float Mb = M;
+#pragma unroll
+    for (int j = 0; j < SB; ++j)
+      if (s0 + j < n_splits) Mb = fmaxf(Mb, ml[j][0]);
+    if (Mb == -INFINITY) continue;
+    if (M != -INFINITY && Mb != M) {
+      const float a = exp2_fast(M - Mb);
+      l *= a;
+      acc *= a;
+    }
+    M = Mb;
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      if (s0 + j >= n_splits || ml[j][0] == -INFINITY) continue;
+      const float wgt = exp2_fast(ml[j][0] - M);
+      l += wgt * ml[j][1];
+      acc += wgt * x[j];
+    }
   }
   const float inv = 1.f / l;
   if (lse != nullptr && c == 0) lse[row] = (M + __log2f(l)) * 0.6931471805599453f;
@@ -795,8 +818,22 @@ static hipError_t launch_d(const AttnPlan& p, AttnArgs a, hipStream_t st) {
   const long long rows = (long long)p.B * p.Hq * p.n;
   const long long threads = rows * (D / 4);
   const long long blocks = (threads + 255) / 256;
-  hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, st, a.part_o,
-                     a.part_ml, a.out, a.lse, rows, p.n_splits);
+  const int n = p.n_splits;
+  if (n <= 2)
+    hipLaunchKernelGGL((attn_combine_kernel<D, 2>), dim3((unsigned)blocks), dim3(256), 0, st, a.part_o, a.part_ml,
+                       a.out, a.lse, rows, n);
+  else if (n <= 4)
+    hipLaunchKernelGGL((attn_combine_kernel<D, 4>), dim3((unsigned)blocks), dim3(256), 0, st, a.part_o, a.part_ml,
+                       a.out, a.lse, rows, n);
+  else if (n <= 8)
+    hipLaunchKernelGGL((attn_combine_kernel<D, 8>), dim3((unsigned)blocks), dim3(256), 0, st, a.part_o, a.part_ml,
+                       a.out, a.lse, rows, n);
+  else if (n <= 16)
+    hipLaunchKernelGGL((attn_combine_kernel<D, 16>), dim3((unsigned)blocks), dim3(256), 0, st, a.part_o, a.part_ml,
+                       a.out, a.lse, rows, n);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<D, 32>), dim3((unsigned)blocks), dim3(256), 0, st, a.part_o, a.part_ml,
+                       a.out, a.lse, rows, n);
   return hipGetLastError();
 }
 

@@ -10,6 +10,7 @@ namespace bda {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;   // one MFMA bf16 operand
 typedef __attribute__((ext_vector_type(16))) float f32x16;   // 32x32 MFMA accumulator
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;  // 16-byte load/store
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
