@@ -351,6 +351,8 @@ int bda_sprint_prune(const void* k, const void* v, const float* conf, const uint
   const void* al[] = {k, v, k_out, v_out};
   for (const void* x : al)
     if (x && !aligned16(x)) return fail(BDA_EINVAL, "k, v, k_out and v_out must be 16-byte aligned");
+  if (((uintptr_t)conf & 3) || ((uintptr_t)kept & 3) || ((uintptr_t)kept_count & 3) || ((uintptr_t)scores & 3))
+    return fail(BDA_EINVAL, "conf, kept, kept_count and scores must be 4-byte aligned");
   const size_t kb = (size_t)B * Hkv * L * d * 2, ob = (size_t)B * Hkv * cap * d * 2, lb = (size_t)B * L * 4;
   if (cap > 0 && (overlap(k_out, ob, k, kb) || overlap(k_out, ob, v, kb) || overlap(v_out, ob, k, kb) ||
                   overlap(v_out, ob, v, kb) || overlap(k_out, ob, v_out, ob)))

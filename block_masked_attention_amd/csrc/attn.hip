@@ -19,6 +19,8 @@
 //                  straight from the S^T accumulator registers: the two
 //                  4-key transpose reads of a lane pick exactly the keys its
 //                  eight P values belong to, so nothing is shuffled.
+#include <atomic>
+
 #include "common.h"
 #include "geometry.h"
 #include "internal.h"
@@ -788,17 +790,18 @@ static hipError_t launch_main(const AttnArgs& a, long long grid, hipStream_t st)
   return hipGetLastError();
 }
 
-// Compute units of the current device (the persistent grid size).
+// Compute units of the current device (the persistent grid size), queried
+// once per device; concurrent first calls store the same value.
 static int device_cus() {
-  static int cus[64];
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 template <int D>

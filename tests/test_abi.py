@@ -154,6 +154,8 @@ def test_sprint_validation():
     assert call(ko=ctypes.c_void_p((1 << 32) + 8)) == 1     # misaligned
     assert call(ko=ctypes.c_void_p((1 << 32) + 4096)) == 1  # k_out inside k
     assert call(kept=ctypes.c_void_p((2 << 32) + 64)) == 1  # kept inside v
+    assert call(conf=ctypes.c_void_p((3 << 32) + 2)) == 1   # misaligned confidence
+    assert call(sc=ctypes.c_void_p((9 << 32) + 1)) == 1     # misaligned scores
 
 
 def test_sprint_kept_count():
