@@ -169,8 +169,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the multi-GPU "
-              "sharding of the path is a design note, not a measured configuration.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the kernels run on one GPU's share "
+              "of the work, and sharding across GPUs is not implemented.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -50,7 +50,7 @@ enum { BDA_BF16 = 0, BDA_F32 = 1 };
 enum {
     BDA_OK = 0,
     BDA_EINVAL = 1,        /* bad pointer, size, shape or parameter          */
-    BDA_EUNSUPPORTED = 2,  /* valid request this build does not implement    */
+    BDA_EUNSUPPORTED = 2,  /* valid request the library does not implement   */
     BDA_EWORKSPACE = 3,    /* workspace missing or smaller than required     */
     BDA_EHIP = 4           /* the HIP runtime reported an error at launch    */
 };
