@@ -57,9 +57,11 @@ def _load():
     lib.oracle_attention_bwd.argtypes = [I, P, P, P, P, P, P, P, P, L, L, L, L, L, L, I]
     lib.oracle_sprint.argtypes = [P, P, P, ctypes.c_double, ctypes.c_double, ctypes.c_double, L, L, L, L, P, P]
     lib.oracle_sprint.restype = L
+    lib.oracle_commit_entropy.argtypes = [P, P, P, ctypes.c_double, ctypes.c_double, L, L, L, L, P, P, I]
     lib.oracle_max_threads.restype = I
     for f in (lib.oracle_mask_shape, lib.oracle_mask, lib.oracle_attention,
-              lib.oracle_commit, lib.oracle_verify, lib.oracle_row_stats, lib.oracle_attention_bwd):
+              lib.oracle_commit, lib.oracle_verify, lib.oracle_row_stats, lib.oracle_attention_bwd,
+              lib.oracle_commit_entropy):
         f.restype = I
     _lib = lib
     return lib
@@ -200,6 +202,52 @@ def row_stats(logits, masked=None, nthreads: int = 0):
     if rc:
         raise ValueError("oracle_row_stats: bad arguments")
     return conf, am, ent, mean
+
+
+def commit_entropy(logits, masked, tokens, bound: float, temperature: float, k_min: int, nthreads: int = 0):
+    """Entropy-bound commit in double on logits [G,R,V].  bound and
+    temperature are fp32 parameters (as the library takes them) used at their
+    double values.  Returns (tokens, masked, entropy [G,R] (NaN where not
+    masked), argmax [G,R] (-1 where not masked)) as new arrays."""
+    lib = _load()
+    lg = _f32(logits)
+    G, R, V = lg.shape
+    m = np.ascontiguousarray(np.asarray(masked, dtype=np.uint8)).copy()
+    t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64)).copy()
+    ent = np.full((G, R), np.nan)
+    am = np.full((G, R), -1, dtype=np.int64)
+    rc = lib.oracle_commit_entropy(_ptr(lg), _ptr(t), _ptr(m), float(np.float32(bound)),
+                                   float(np.float32(temperature)), k_min, G, R, V, _ptr(ent), _ptr(am), nthreads)
+    if rc:
+        raise ValueError("oracle_commit_entropy: bad arguments")
+    return t, m, ent, am
+
+
+def adaptive_stop_step(argmax, prev, stable, frozen, mean_entropy, stability_threshold: int,
+                       confidence_threshold: float):
+    """One step of adaptive stopping ([DGemma] "Adaptive stopping"), per
+    example g of argmax [G,R]: an example already frozen keeps its state;
+    otherwise stable[g] counts the consecutive steps whose argmax equals the
+    previous step's (reset to 0 on any change; prev = -1 counts as a change),
+    prev becomes this step's argmax, and the example freezes once stable[g]
+    >= stability_threshold and mean_entropy[g] < confidence_threshold (a
+    float32 parameter).  Plain loops; returns new (prev, stable, frozen)."""
+    argmax = np.asarray(argmax, dtype=np.int64)
+    prev = np.array(prev, dtype=np.int64, copy=True)
+    stable = np.array(stable, dtype=np.int64, copy=True)
+    frozen = np.array(frozen, dtype=np.uint8, copy=True)
+    thr = float(np.float32(confidence_threshold))
+    G, R = argmax.shape
+    for g in range(G):
+        if frozen[g]:
+            continue
+        same = all(int(argmax[g, r]) == int(prev[g, r]) for r in range(R))
+        stable[g] = stable[g] + 1 if same else 0
+        for r in range(R):
+            prev[g, r] = argmax[g, r]
+        if stable[g] >= stability_threshold and float(np.float32(mean_entropy[g])) < thr:
+            frozen[g] = 1
+    return prev, stable, frozen
 
 
 def tile_class(M: np.ndarray, q0: int, q1: int, k0: int, k1: int) -> int:

@@ -492,6 +492,81 @@ int oracle_row_stats(const float* logits, const uint8_t* masked, double* conf, i
 }
 
 /*
+ * Entropy-bound commit ([DGemma] "Schedulers", EntropyBoundScheduler: commit
+ * the lowest-entropy positions whose joint entropy stays within the bound).
+ * For each masked row t of group g: p_j = softmax(l_j / T) with T =
+ * temperature, H_t = -sum_j p_j log p_j in nats (term by term), a_t = lowest
+ * j reaching the largest logit.  The group's masked rows are ordered by
+ * (H ascending, row ascending); with S_j the sum of the first j entropies,
+ * the first n rows are committed, n = max(min(k_min, #masked),
+ * max{ j : S_j <= bound }): tokens = a, masked = 0.  Joint entropy is read as
+ * the sum of the per-position entropies (independent positions).
+ * entropy[t] / argmax[t] are written for masked rows.  Returns 0, 1 on a bad
+ * argument.
+ */
+static const double *g_ent_key;
+static int ent_cmp(const void *x, const void *y)
+{
+    const long a = *(const long *)x, b = *(const long *)y;
+    const double ha = g_ent_key[a], hb = g_ent_key[b];
+    if (ha < hb) return -1;
+    if (ha > hb) return 1;
+    return (a > b) - (a < b);
+}
+
+int oracle_commit_entropy(const float* logits, int64_t* tokens, uint8_t* masked, double bound, double temperature,
+                          long k_min, long G, long R, long V, double* entropy, int64_t* argmax, int nthreads)
+{
+    if (G < 0 || R < 0 || V <= 0 || k_min < 0 || !(temperature > 0.0)) return 1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long t = 0; t < G * R; ++t) {
+        if (!masked[t]) continue;
+        const float* row = logits + t * V;
+        double m = (double)row[0];
+        long idx = 0;
+        for (long j = 1; j < V; ++j)
+            if ((double)row[j] > m) { m = (double)row[j]; idx = j; }
+        double Z = 0.0;
+        for (long j = 0; j < V; ++j) Z += exp(((double)row[j] - m) / temperature);
+        double H = 0.0;
+        for (long j = 0; j < V; ++j) {
+            const double pj = exp(((double)row[j] - m) / temperature) / Z;
+            if (pj > 0.0) H -= pj * log(pj);
+        }
+        entropy[t] = H;
+        argmax[t] = idx;
+    }
+    long* order = (long*)malloc(sizeof(long) * (size_t)(R > 0 ? R : 1));
+    if (!order) return 1;
+    for (long g = 0; g < G; ++g) {
+        long n = 0;
+        for (long r = 0; r < R; ++r)
+            if (masked[g * R + r]) order[n++] = g * R + r;
+        g_ent_key = entropy;
+        qsort(order, (size_t)n, sizeof(long), ent_cmp);
+        long take = 0;
+        double sum = 0.0;
+        for (long j = 0; j < n; ++j) {
+            sum += entropy[order[j]];
+            if (sum <= bound) take = j + 1;
+            else break;
+        }
+        if (take < (k_min < n ? k_min : n)) take = k_min < n ? k_min : n;
+        for (long j = 0; j < take; ++j) {
+            tokens[order[j]] = argmax[order[j]];
+            masked[order[j]] = 0;
+        }
+    }
+    free(order);
+    return 0;
+}
+
+/*
  * SPRINT sparse prefix retention ([LLaDA] "SPRINT": the cache is pruned once
  * at the start of a block).  For batch b and prefix position i:
  *   n_i   = || k_{b,.,i,.} ||_2 over all kv heads and channels,

@@ -527,3 +527,110 @@ def test_sprint_equal_confidence_ranks_by_key_norm():
     assert np.allclose(sc[0], 0.5 * n64 / n64.mean() + 0.5 * float(np.float32(0.4)), rtol=1e-12)
     order = sorted(range(L), key=lambda i: (-norms[i], i))[:K]
     assert K == 8 and list(kept[0, :K]) == sorted(order)                  # ties (the 9s, 5s) by position
+
+
+# ---- Entropy-bound commit ([DGemma] Schedulers, EntropyBoundScheduler)
+
+def _entropy_commit_brute(logits, masked, bound, temperature, k_min):
+    """Restatement with scipy's softmax and entropy, Python sorting and sums."""
+    import scipy.special
+    import scipy.stats
+    G, R, V = logits.shape
+    T = float(np.float32(temperature))
+    b = float(np.float32(bound))
+    committed = np.zeros((G, R), bool)
+    for g in range(G):
+        rows = [r for r in range(R) if masked[g, r]]
+        H = {r: float(scipy.stats.entropy(scipy.special.softmax(logits[g, r].astype(np.float64) / T))) for r in rows}
+        order = sorted(rows, key=lambda r: (H[r], r))
+        n, acc = 0, 0.0
+        for j, r in enumerate(order):
+            acc += H[r]
+            if acc <= b:
+                n = j + 1
+            else:
+                break
+        n = max(n, min(k_min, len(rows)))
+        for r in order[:n]:
+            committed[g, r] = True
+    return committed
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_entropy_commit_matches_restatement(seed):
+    g = np.random.default_rng(70 + seed)
+    G, R, V = 3, 9, 50
+    logits = (g.standard_normal((G, R, V)) * g.uniform(0.5, 6.0, (G, R, 1))).astype(np.float32)
+    masked = (g.uniform(size=(G, R)) < 0.7).astype(np.uint8)
+    bound, T, k_min = float(g.uniform(0.5, 8.0)), float(g.choice([0.4, 0.8, 1.0, 1.7])), int(g.integers(0, 3))
+    tokens = np.full((G, R), -1, np.int64)
+    t, m, ent, am = oracle.commit_entropy(logits, masked, tokens, bound, T, k_min)
+    want = _entropy_commit_brute(logits, masked, bound, T, k_min)
+    assert np.array_equal((masked == 1) & (m == 0), want)
+    assert np.array_equal(t[want], logits.argmax(-1)[want])          # argmax: lowest index of the max
+    assert (t[~want] == -1).all() and (m[~want] == masked[~want]).all()
+
+
+def test_entropy_commit_temperature_and_closed_forms():
+    g = np.random.default_rng(80)
+    G, R, V = 2, 6, 64
+    logits = (g.standard_normal((G, R, V)) * 3).astype(np.float32)
+    masked = np.ones((G, R), np.uint8)
+    tok = np.full((G, R), -1, np.int64)
+    # softmax(l / 0.5) is softmax((2 l) / 1): same entropies
+    _, _, e_half, _ = oracle.commit_entropy(logits, masked, tok, 1.0, 0.5, 0)
+    _, _, e_two, _ = oracle.commit_entropy(2 * logits, masked, tok, 1.0, 1.0, 0)
+    assert np.allclose(e_half, e_two, rtol=1e-14, atol=0)
+    # uniform rows: H = log V at any temperature; ties go to the lower row
+    uni = np.zeros((1, 5, V), np.float32)
+    m1 = np.ones((1, 5), np.uint8)
+    t, m, e, _ = oracle.commit_entropy(uni, m1, np.full((1, 5), -1, np.int64), 2.5 * np.log(V), 0.8, 0)
+    assert np.allclose(e, np.log(V), rtol=1e-14)
+    assert list(m[0]) == [0, 0, 1, 1, 1] and list(t[0, :2]) == [0, 0]
+    # bound below every entropy: exactly min(k_min, #masked) rows, the lowest-entropy ones
+    peaked = np.zeros((1, 4, V), np.float32)
+    for r, gap in enumerate([1.0, 9.0, 3.0, 30.0]):
+        peaked[0, r, 7 + r] = gap                                     # larger gap, lower entropy
+    _, m, e, _ = oracle.commit_entropy(peaked, np.ones((1, 4), np.uint8), np.full((1, 4), -1, np.int64), -1.0, 1.0, 2)
+    assert list(m[0]) == [1, 0, 1, 0]
+    _, m, _, _ = oracle.commit_entropy(peaked, np.ones((1, 4), np.uint8), np.full((1, 4), -1, np.int64), -1.0, 1.0, 0)
+    assert list(m[0]) == [1, 1, 1, 1]
+    # a bound above the total commits every masked row
+    _, m, e, _ = oracle.commit_entropy(peaked, np.array([[1, 0, 1, 1]], np.uint8), np.full((1, 4), -1, np.int64),
+                                       1e9, 1.0, 0)
+    assert list(m[0]) == [0, 0, 0, 0] and np.isnan(e[0, 1])
+    # single-peak closed form: H = log Z - (gap e^gap) / Z, Z = e^gap + V - 1
+    gap = 3.0
+    Z = np.exp(gap) + V - 1
+    assert abs(e[0, 2] - (np.log(Z) - gap * np.exp(gap) / Z)) < 1e-12
+
+
+def test_adaptive_stop_steps():
+    G, R = 3, 4
+    prev = np.full((G, R), -1, np.int64)
+    stable = np.zeros(G, np.int64)
+    frozen = np.zeros(G, np.uint8)
+    a0 = np.arange(G * R).reshape(G, R)
+    low, high = np.array([0.001, 0.001, 0.1]), np.array([0.001, 0.01, 0.001])
+    # first step: prev unset, nothing is stable yet
+    prev, stable, frozen = oracle.adaptive_stop_step(a0, prev, stable, frozen, low, 1, 0.005)
+    assert list(stable) == [0, 0, 0] and list(frozen) == [0, 0, 0] and np.array_equal(prev, a0)
+    # unchanged argmax: stable 1; example 0 freezes (entropy below), 1 not (0.01), 2 not (0.1)
+    a1 = a0.copy()
+    a1[1, 3] = a0[1, 3]                                               # unchanged
+    prev, stable, frozen = oracle.adaptive_stop_step(a1, prev, stable, frozen, high * 0 + [0.001, 0.01, 0.1], 1, 0.005)
+    assert list(stable) == [1, 1, 1] and list(frozen) == [1, 0, 0]
+    # example 1 changes one position: counter resets; example 2 stays and its entropy drops
+    a2 = a1.copy()
+    a2[1, 0] += 100
+    a2[0, 0] += 100                                                   # example 0 is frozen: ignored
+    prev, stable, frozen = oracle.adaptive_stop_step(a2, prev, stable, frozen, np.array([0.5, 0.001, 0.001]), 1, 0.005)
+    assert list(stable) == [1, 0, 2] and list(frozen) == [1, 0, 1]
+    assert prev[0, 0] == a1[0, 0] and prev[1, 0] == a2[1, 0]
+    # a threshold of 2 needs two unchanged steps; equality with the confidence threshold does not freeze
+    p, s, f = oracle.adaptive_stop_step(a0[:1], a0[:1], [0], [0], [0.0], 2, 0.005)
+    assert list(s) == [1] and list(f) == [0]
+    p, s, f = oracle.adaptive_stop_step(a0[:1], p, s, f, [0.0], 2, 0.005)
+    assert list(s) == [2] and list(f) == [1]
+    p, s, f = oracle.adaptive_stop_step(a0[:1], a0[:1], [5], [0], [np.float32(0.005)], 1, 0.005)
+    assert list(f) == [0]
