@@ -385,6 +385,23 @@ def secondary(bda, synth, torch, dev, args):
                         "algorithmic_bytes": byts}
     log(f"[bench] row_stats: {res['row_stats']}")
 
+    # ---- entropy-bound commit on the same logits (bound 14 nats per group,
+    # temperature 1, at least one commit)
+    ews = torch.empty(bda.lib.bda_commit_entropy_workspace_bytes(G, R, V), dtype=torch.uint8, device=dev)
+
+    def erun(i):
+        bda.commit_entropy(sets[i % 3], tokens, masked, 14.0, 1.0, 1, workspace=ews)
+
+    mean, med = time_launches(erun, iters, 5, pre=pre)
+    torch.cuda.synchronize()
+    n_commit = int(G * R - masked.sum().item())
+    res["entropy_commit"] = {"G": G, "R": R, "V": V, "entropy_bound": 14.0, "us_per_call": round(mean * 1e3, 2),
+                             "committed_per_call": n_commit,
+                             "GB/s": round(byts / (mean * 1e-3) / 1e9, 1),
+                             "hbm_frac": round(byts / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                             "algorithmic_bytes": byts}
+    log(f"[bench] entropy_commit: {res['entropy_commit']}")
+
     # ---- SPRINT pruning of the multimodal prefix (B=2, 8 kv heads, 4096
     # positions: 3080 image, 1016 text; keep 0.8 of the image, all text), and
     # one decode step of a 28-row block over the pruned vs the full cache.

@@ -27,7 +27,7 @@ _ENTRY_POINTS = (
     "bda_last_error", "bda_version", "bda_row_stats", "bda_row_stats_workspace_bytes",
     "bda_attn_fwd_lse", "bda_attn_bwd", "bda_attn_bwd_workspace_bytes", "bda_sprint_prune",
     "bda_sprint_workspace_bytes", "bda_sprint_kept_count", "bda_attn_fwd_varlen", "bda_kv_append",
-    "bda_verify_crop",
+    "bda_verify_crop", "bda_commit_entropy", "bda_commit_entropy_workspace_bytes", "bda_adaptive_stop",
 )
 
 
@@ -53,6 +53,12 @@ def _load():
     L.bda_kv_append.restype = I
     L.bda_verify_crop.argtypes = [P, I, P, P, P, P, I, I, I, I, P, S, P]
     L.bda_verify_crop.restype = I
+    L.bda_commit_entropy.argtypes = [P, I, P, P, F, F, I, I, I, I, P, S, P]
+    L.bda_commit_entropy.restype = I
+    L.bda_commit_entropy_workspace_bytes.argtypes = [I, I, I]
+    L.bda_commit_entropy_workspace_bytes.restype = S
+    L.bda_adaptive_stop.argtypes = [P, P, P, P, P, I, I, I, F, P, P]
+    L.bda_adaptive_stop.restype = I
     L.bda_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, S, P]
     L.bda_attn_bwd.restype = I
     L.bda_attn_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
@@ -295,6 +301,53 @@ def verify_crop(logits, drafts, kv_len, kv_cap: int, argmax_out=None, accept_len
     if rc:
         raise BdaError(rc, "bda_verify_crop")
     return am, acc
+
+
+def commit_entropy(logits, tokens, masked, entropy_bound: float, temperature: float = 1.0, k_min: int = 1,
+                   workspace=None):
+    """Entropy-bound commit on logits [G,R,V] (bf16 or fp32): updates
+    ``tokens`` (int64 [G,R]) and ``masked`` (uint8 [G,R]) in place."""
+    if logits.dim() != 3:
+        raise ValueError("logits must be [G, R, V]")
+    G, R, V = logits.shape
+    dt = {torch.bfloat16: BF16, torch.float32: F32}.get(logits.dtype)
+    if dt is None:
+        raise ValueError("logits must be bfloat16 or float32")
+    if tokens.dtype != torch.int64 or masked.dtype != torch.uint8 or tuple(tokens.shape) != (G, R) \
+            or tuple(masked.shape) != (G, R):
+        raise ValueError("tokens must be int64 [G, R] and masked uint8 [G, R]")
+    dev = _check_dev(logits, tokens, masked)
+    need = int(lib.bda_commit_entropy_workspace_bytes(G, R, V))
+    ws = _workspace(need, dev, workspace)
+    rc = lib.bda_commit_entropy(_ptr(logits), dt, _ptr(tokens), _ptr(masked), entropy_bound, temperature, k_min,
+                                G, R, V, _ptr(ws), need, _stream(dev))
+    if rc:
+        raise BdaError(rc, "bda_commit_entropy")
+
+
+def adaptive_stop(argmax, prev_argmax, stable_steps, frozen, mean_entropy, stability_threshold: int = 1,
+                  confidence_threshold: float = 0.005, n_frozen=None):
+    """One adaptive-stopping step on device state (updated in place):
+    argmax / prev_argmax int64 [G,R], stable_steps int32 [G], frozen uint8
+    [G], mean_entropy float32 [G]; n_frozen (int32 [1]) if given receives the
+    number of frozen examples."""
+    G = frozen.shape[0]
+    R = argmax.shape[1] if argmax.dim() == 2 else 0
+    if argmax.dtype != torch.int64 or prev_argmax.dtype != torch.int64 or tuple(argmax.shape) != (G, R) \
+            or tuple(prev_argmax.shape) != (G, R):
+        raise ValueError("argmax and prev_argmax must be int64 [G, R]")
+    if stable_steps.dtype != torch.int32 or frozen.dtype != torch.uint8 or mean_entropy.dtype != torch.float32:
+        raise ValueError("stable_steps int32 [G], frozen uint8 [G], mean_entropy float32 [G]")
+    if tuple(stable_steps.shape) != (G,) or tuple(mean_entropy.shape) != (G,):
+        raise ValueError("stable_steps and mean_entropy must be [G]")
+    if n_frozen is not None and (n_frozen.dtype != torch.int32 or n_frozen.numel() < 1):
+        raise ValueError("n_frozen must be int32 with at least one element")
+    dev = _check_dev(argmax, prev_argmax, stable_steps, frozen, mean_entropy, n_frozen)
+    rc = lib.bda_adaptive_stop(_ptr(argmax), _ptr(prev_argmax), _ptr(stable_steps), _ptr(frozen),
+                               _ptr(mean_entropy), G, R, stability_threshold, confidence_threshold, _ptr(n_frozen),
+                               _stream(dev))
+    if rc:
+        raise BdaError(rc, "bda_adaptive_stop")
 
 
 def verify(logits, drafts, workspace=None):

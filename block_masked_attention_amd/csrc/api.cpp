@@ -182,6 +182,61 @@ int bda_commit(const void* logits, int dtype, int64_t* tokens, uint8_t* masked, 
 
 size_t bda_verify_workspace_bytes(int B, int R, int V) { return bda_commit_workspace_bytes(B, R, V); }
 
+size_t bda_commit_entropy_workspace_bytes(int G, int R, int V) { return bda_commit_workspace_bytes(G, R, V); }
+
+int bda_commit_entropy(const void* logits, int dtype, int64_t* tokens, uint8_t* masked, float entropy_bound,
+                       float temperature, int k_min, int G, int R, int V, void* workspace, size_t ws_bytes,
+                       void* stream) {
+  if (int e = check_logits(logits, dtype, G, R, V, "G")) return e;
+  if (k_min < 0) return fail(BDA_EINVAL, "k_min must be >= 0");
+  if (isnan(entropy_bound)) return fail(BDA_EINVAL, "entropy_bound is NaN");
+  if (!(temperature > 0.f) || isinf(temperature)) return fail(BDA_EINVAL, "temperature must be finite and > 0");
+  if (R > bda::commit_entropy_max_rows())
+    return fail(BDA_EUNSUPPORTED, "R above %d rows per group", bda::commit_entropy_max_rows());
+  const size_t rows = (size_t)G * R;
+  if (rows == 0) return ok();
+  if (!tokens || !masked) return fail(BDA_EINVAL, "tokens and masked must be non-NULL");
+  const size_t lbytes = rows * V * (dtype == BDA_BF16 ? 2 : 4);
+  if (overlap(tokens, rows * 8, logits, lbytes) || overlap(masked, rows, logits, lbytes) ||
+      overlap(tokens, rows * 8, masked, rows))
+    return fail(BDA_EINVAL, "tokens, masked and logits must not overlap");
+  bda::CommitPlan p;
+  bda::commit_make_plan(G, R, V, dtype, &p);
+  if (!workspace || ws_bytes < p.ws_bytes)
+    return fail(BDA_EWORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_bytes,
+                workspace ? ws_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(BDA_EINVAL, "workspace must be 16-byte aligned");
+  if (overlap(workspace, p.ws_bytes, logits, lbytes) || overlap(workspace, p.ws_bytes, tokens, rows * 8) ||
+      overlap(workspace, p.ws_bytes, masked, rows))
+    return fail(BDA_EINVAL, "workspace overlaps a tensor argument");
+  hipError_t e = bda::commit_entropy_launch(p, logits, tokens, masked, entropy_bound, temperature, k_min, workspace,
+                                            (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BDA_EHIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int bda_adaptive_stop(const int64_t* argmax, int64_t* prev_argmax, int32_t* stable_steps, uint8_t* frozen,
+                      const float* mean_entropy, int G, int R, int stability_threshold,
+                      float confidence_threshold, int32_t* n_frozen, void* stream) {
+  if (G < 0 || R < 0) return fail(BDA_EINVAL, "G and R must be >= 0");
+  if (stability_threshold < 0) return fail(BDA_EINVAL, "stability_threshold must be >= 0");
+  if (isnan(confidence_threshold)) return fail(BDA_EINVAL, "confidence_threshold is NaN");
+  if (G == 0 && !n_frozen) return ok();
+  if (G > 0 && (!stable_steps || !frozen || !mean_entropy || (R > 0 && (!argmax || !prev_argmax))))
+    return fail(BDA_EINVAL, "argmax, prev_argmax, stable_steps, frozen and mean_entropy must be non-NULL");
+  const size_t rows = (size_t)G * R;
+  if (((uintptr_t)argmax & 7) || ((uintptr_t)prev_argmax & 7) || ((uintptr_t)stable_steps & 3) ||
+      ((uintptr_t)mean_entropy & 3) || ((uintptr_t)n_frozen & 3))
+    return fail(BDA_EINVAL, "arguments must be aligned to their element size");
+  if (rows && (overlap(prev_argmax, rows * 8, argmax, rows * 8) || overlap(stable_steps, (size_t)G * 4, prev_argmax, rows * 8) ||
+               overlap(frozen, (size_t)G, prev_argmax, rows * 8)))
+    return fail(BDA_EINVAL, "outputs must not overlap each other or argmax");
+  hipError_t e = bda::adaptive_stop_launch(argmax, prev_argmax, stable_steps, frozen, mean_entropy, G, R,
+                                           stability_threshold, confidence_threshold, n_frozen, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BDA_EHIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 static int verify_impl(const void* logits, int dtype, const int64_t* drafts, int64_t* argmax_out,
                        int32_t* accept_len, int32_t* kv_len, int kv_cap, int B, int R, int V, void* workspace,
                        size_t ws_bytes, void* stream) {

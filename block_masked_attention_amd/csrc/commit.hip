@@ -49,7 +49,7 @@ struct Stat {
   float t;
 };
 
-__device__ __forceinline__ Stat merge(Stat x, Stat y, int kind) {
+__device__ __forceinline__ Stat merge(Stat x, Stat y, int kind, float c = kLog2e) {
   Stat r;
   r.m = fmaxf(x.m, y.m);
   r.a = x.m > y.m ? x.a : (y.m > x.m ? y.a : min(x.a, y.a));
@@ -58,8 +58,8 @@ __device__ __forceinline__ Stat merge(Stat x, Stat y, int kind) {
   if (kind != kArgmax && r.m != -INFINITY) {
     // a side whose maximum is -inf holds no value and contributes nothing
     const float dx = x.m - r.m, dy = y.m - r.m;
-    const float ax = x.m == -INFINITY ? 0.f : exp2_fast(dx * kLog2e);
-    const float ay = y.m == -INFINITY ? 0.f : exp2_fast(dy * kLog2e);
+    const float ax = x.m == -INFINITY ? 0.f : exp2_fast(dx * c);
+    const float ay = y.m == -INFINITY ? 0.f : exp2_fast(dy * c);
     r.z = x.z * ax + y.z * ay;
     if (kind == kWithZT)
       r.t = (x.m == -INFINITY ? 0.f : ax * (x.t + dx * x.z)) + (y.m == -INFINITY ? 0.f : ay * (y.t + dy * y.z));
@@ -75,7 +75,7 @@ __device__ __forceinline__ float load_one(const void* row, int j) {
 
 // Fold 8 values (indices base..base+7, increasing) into a lane's state.
 template <int KIND>
-__device__ __forceinline__ void fold8(Stat& s, const float (&x)[8], int base) {
+__device__ __forceinline__ void fold8(Stat& s, const float (&x)[8], int base, float c) {
   float lm = x[0];
 #pragma unroll
   for (int e = 1; e < 8; ++e) lm = fmaxf(lm, x[e]);
@@ -88,7 +88,7 @@ __device__ __forceinline__ void fold8(Stat& s, const float (&x)[8], int base) {
         s.z = 0.f;
         s.t = 0.f;
       } else {
-        const float d = s.m - lm, a = exp2_fast(d * kLog2e);
+        const float d = s.m - lm, a = exp2_fast(d * c);
         if (KIND == kWithZT) s.t = a * (s.t + d * s.z);
         s.z *= a;
       }
@@ -97,11 +97,11 @@ __device__ __forceinline__ void fold8(Stat& s, const float (&x)[8], int base) {
     s.a = base + idx;
   }
   if (KIND != kArgmax && s.m != -INFINITY) {
-    const float nb = -s.m * kLog2e;
+    const float nb = -s.m * c;
     float acc = 0.f, acct = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float p = exp2_fast(fmaf(x[e], kLog2e, nb));
+      const float p = exp2_fast(fmaf(x[e], c, nb));
       acc += p;
       if (KIND == kWithZT) acct = fmaf(p, x[e] == -INFINITY ? 0.f : x[e] - s.m, acct);   // -inf: padding
     }
@@ -114,7 +114,7 @@ template <bool BF16, int KIND>
 __global__ __launch_bounds__(kCommitThreads) void stream_kernel(const void* __restrict__ logits,
                                                                 const uint8_t* __restrict__ masked,
                                                                 Partial* __restrict__ part, int V,
-                                                                int n_chunks, int vec_ok) {
+                                                                int n_chunks, int vec_ok, float xs) {
   constexpr int VPT = kChunk / (8 * kCommitThreads);   // 8-value vectors per thread
   const int bid = blockIdx.x;
   const int t = bid / n_chunks;
@@ -173,13 +173,13 @@ __global__ __launch_bounds__(kCommitThreads) void stream_kernel(const void* __re
     }
     // pass 2: Z (and T) against that maximum
     if (KIND != kArgmax) {
-      const float nb = -s.m * kLog2e;
+      const float nb = -s.m * xs;
       float acc[4] = {0.f, 0.f, 0.f, 0.f}, acct[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int v = 0; v < VPT; ++v)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float p = exp2_fast(fmaf(x[v][e], kLog2e, nb));
+          const float p = exp2_fast(fmaf(x[v][e], xs, nb));
           acc[e & 3] += p;
           if (KIND == kWithZT) acct[e & 3] = fmaf(p, x[v][e] - s.m, acct[e & 3]);
         }
@@ -211,14 +211,14 @@ __global__ __launch_bounds__(kCommitThreads) void stream_kernel(const void* __re
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = base + e < c1 ? load_one<BF16>(row, base + e) : -INFINITY;
       }
-      fold8<KIND>(s, x, base);
+      fold8<KIND>(s, x, base, xs);
     }
   } else {
     for (int base = c0 + 8 * tid; base < c1; base += 8 * kCommitThreads) {
       float x[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = base + e < c1 ? load_one<BF16>(row, base + e) : -INFINITY;
-      fold8<KIND>(s, x, base);
+      fold8<KIND>(s, x, base, xs);
     }
   }
   // -INFINITY padding never wins a strict comparison, and contributes 0 to Z
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(kCommitThreads) void stream_kernel(const void* __re
     o.z = __shfl_xor(s.z, off);
     o.a = __shfl_xor(s.a, off);
     o.t = __shfl_xor(s.t, off);
-    s = merge(s, o, KIND);
+    s = merge(s, o, KIND, xs);
   }
   __shared__ Stat wst[kCommitThreads / 64];
   if ((tid & 63) == 0) wst[tid >> 6] = s;
@@ -239,7 +239,7 @@ __global__ __launch_bounds__(kCommitThreads) void stream_kernel(const void* __re
   if (tid == 0) {
     Stat r = wst[0];
 #pragma unroll
-    for (int w = 1; w < kCommitThreads / 64; ++w) r = merge(r, wst[w], KIND);
+    for (int w = 1; w < kCommitThreads / 64; ++w) r = merge(r, wst[w], KIND, xs);
     Partial p;
     p.m = r.m;
     p.z = r.z;
@@ -249,12 +249,13 @@ __global__ __launch_bounds__(kCommitThreads) void stream_kernel(const void* __re
   }
 }
 
-__device__ __forceinline__ Stat row_stat(const Partial* part, size_t t, int n_chunks, int kind) {
+__device__ __forceinline__ Stat row_stat(const Partial* part, size_t t, int n_chunks, int kind,
+                                        float c = kLog2e) {
   const Partial& q0 = part[t * n_chunks];
   Stat s{q0.m, q0.z, q0.a, q0.t};
-  for (int c = 1; c < n_chunks; ++c) {
-    const Partial& q = part[t * n_chunks + c];
-    s = merge(s, Stat{q.m, q.z, q.a, q.t}, kind);
+  for (int ci = 1; ci < n_chunks; ++ci) {
+    const Partial& q = part[t * n_chunks + ci];
+    s = merge(s, Stat{q.m, q.z, q.a, q.t}, kind, c);
   }
   return s;
 }
@@ -386,6 +387,126 @@ __global__ __launch_bounds__(kCommitThreads) void stats_finalize_kernel(
   if (threadIdx.x == 0 && mean_entropy) mean_entropy[g] = cnt > 0 ? hsum / (float)cnt : 0.f;
 }
 
+// Entropy-bound commit (the EntropyBoundScheduler of the DiffusionGemma
+// pipeline page, "Schedulers"), one workgroup per group of R <= kEntMaxR
+// rows: every masked row's entropy H (nats, of softmax(l / T)) and argmax go
+// to LDS; each masked row's rank among them by (H ascending, row ascending)
+// is counted; the ranked entropies are summed in rank order and the first n
+// ranks are committed, n = max(min(k_min, #masked), the longest prefix whose
+// sum stays <= bound).  inv_t = 1 / T (the streamed T sums are in logit
+// units).
+constexpr int kEntMaxR = 4096;
+
+__global__ __launch_bounds__(kCommitThreads) void commit_entropy_finalize_kernel(
+    const Partial* __restrict__ part, int n_chunks, int64_t* __restrict__ tokens, uint8_t* __restrict__ masked,
+    float bound, int k_min, int R, float c, float inv_t) {
+  __shared__ float sh[kEntMaxR];
+  __shared__ float sorted_h[kEntMaxR];
+  __shared__ int sa[kEntMaxR];
+  __shared__ int red[kCommitThreads / 64];
+  __shared__ int take_n;
+  const int g = blockIdx.x, tid = threadIdx.x;
+  const size_t base = (size_t)g * R;
+  int nm = 0;
+  for (int r = tid; r < R; r += kCommitThreads) {
+    float h = INFINITY;                          // unmasked: never ranked
+    int a = -1;
+    if (masked[base + r]) {
+      const Stat st = row_stat(part, base + r, n_chunks, kWithZT, c);
+      h = logf(st.z) - (st.t * inv_t) / st.z;
+      a = st.a;
+      nm += 1;
+    }
+    sh[r] = h;
+    sa[r] = a;
+  }
+  const int nmask = block_sum(nm, red);          // (its barriers also publish sh, sa)
+  for (int r = tid; r < R; r += kCommitThreads) {
+    if (sa[r] < 0) continue;
+    const float h = sh[r];
+    int rank = 0;
+    for (int o = 0; o < R; ++o) {
+      const float ho = sh[o];
+      rank += (ho < h) || (ho == h && o < r);
+    }
+    sorted_h[rank] = h;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float acc = 0.f;
+    int n = 0;
+    for (int j = 0; j < nmask; ++j) {
+      acc += sorted_h[j];
+      if (acc <= bound) n = j + 1;
+      else break;
+    }
+    take_n = max(n, min(k_min, nmask));
+  }
+  __syncthreads();
+  const int n = take_n;
+  for (int r = tid; r < R; r += kCommitThreads) {
+    if (sa[r] < 0) continue;
+    const float h = sh[r];
+    int rank = 0;
+    for (int o = 0; o < R && rank < n; ++o) {
+      const float ho = sh[o];
+      rank += (ho < h) || (ho == h && o < r);
+    }
+    if (rank < n) {
+      tokens[base + r] = sa[r];
+      masked[base + r] = 0;
+    }
+  }
+}
+
+// Adaptive stopping (the DiffusionGemma pipeline page, "Adaptive stopping"),
+// one workgroup for all G examples, a wavefront per example at a time: an
+// example already frozen keeps its state; otherwise stable[g] counts the
+// consecutive steps whose argmax equals the previous step's (any change
+// resets it to 0), prev takes this step's argmax, and the example freezes
+// once stable[g] >= stability and mean_entropy[g] < conf_thr.  n_frozen
+// (optional) receives the number of frozen examples after the step.
+__global__ __launch_bounds__(1024) void adaptive_stop_kernel(const int64_t* __restrict__ argmax,
+                                                             int64_t* __restrict__ prev, int32_t* __restrict__ stable,
+                                                             uint8_t* __restrict__ frozen,
+                                                             const float* __restrict__ mean_entropy, int G, int R,
+                                                             int stability, float conf_thr,
+                                                             int32_t* __restrict__ n_frozen) {
+  __shared__ int cnt[16];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int nf = 0;
+  for (int g = w; g < G; g += 16) {
+    int fz = frozen[g];
+    if (!fz) {
+      bool changed = false;
+      for (int r = lane; r < R; r += 64) {
+        const size_t t = (size_t)g * R + r;
+        const int64_t a = argmax[t];
+        changed |= a != prev[t];
+        prev[t] = a;
+      }
+      changed = __any(changed);
+      if (lane == 0) {
+        const int s = changed ? 0 : stable[g] + 1;
+        stable[g] = s;
+        if (s >= stability && mean_entropy[g] < conf_thr) {
+          frozen[g] = 1;
+          fz = 1;
+        }
+      }
+      fz = __shfl(fz, 0);
+    }
+    nf += fz;
+  }
+  if (lane == 0) cnt[w] = nf;
+  __syncthreads();
+  if (threadIdx.x == 0 && n_frozen) {
+    int s = 0;
+    for (int i = 0; i < 16; ++i) s += cnt[i];
+    *n_frozen = s;
+  }
+}
+
 // ----------------------------------------------------------------------------
 // host side
 // ----------------------------------------------------------------------------
@@ -424,15 +545,15 @@ static bool vec_ok(const void* logits, int V, int dtype) {
 
 template <int KIND>
 static hipError_t launch_stream(const CommitPlan& p, const void* logits, const uint8_t* masked,
-                                Partial* part, hipStream_t st) {
+                                Partial* part, hipStream_t st, float c = kLog2e) {
   const long long grid = (long long)p.G * p.R * p.n_chunks;
   const int vo = vec_ok(logits, p.V, p.dtype);
   if (p.dtype == 0)
     hipLaunchKernelGGL((stream_kernel<true, KIND>), dim3((unsigned)grid), dim3(kCommitThreads), 0,
-                       st, logits, masked, part, p.V, p.n_chunks, vo);
+                       st, logits, masked, part, p.V, p.n_chunks, vo, c);
   else
     hipLaunchKernelGGL((stream_kernel<false, KIND>), dim3((unsigned)grid), dim3(kCommitThreads), 0,
-                       st, logits, masked, part, p.V, p.n_chunks, vo);
+                       st, logits, masked, part, p.V, p.n_chunks, vo, c);
   return hipGetLastError();
 }
 
@@ -487,6 +608,38 @@ hipError_t stats_launch(const CommitPlan& p, const void* logits, const uint8_t* 
   }
   hipLaunchKernelGGL(stats_finalize_kernel, dim3(p.G), dim3(kCommitThreads), 0, st, part, p.n_chunks,
                      masked, p.R, conf, argmax_out, entropy, mean_entropy);
+  return hipGetLastError();
+}
+
+}  // namespace bda
+
+namespace bda {
+
+hipError_t commit_entropy_launch(const CommitPlan& p, const void* logits, int64_t* tokens, uint8_t* masked,
+                                 float bound, float temperature, int k_min, void* ws, hipStream_t st) {
+  if ((long long)p.G * p.R == 0) return hipSuccess;
+  Partial* part;
+  float* rowp;
+  int* rowa;
+  uint8_t* rowf;
+  carve(p, ws, &part, &rowp, &rowa, &rowf);
+  (void)hipGetLastError();
+  const float c = kLog2e / temperature;
+  hipError_t e = launch_stream<kWithZT>(p, logits, masked, part, st, c);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(commit_entropy_finalize_kernel, dim3(p.G), dim3(kCommitThreads), 0, st, part, p.n_chunks,
+                     tokens, masked, bound, k_min, p.R, c, 1.f / temperature);
+  return hipGetLastError();
+}
+
+int commit_entropy_max_rows() { return kEntMaxR; }
+
+hipError_t adaptive_stop_launch(const int64_t* argmax, int64_t* prev, int32_t* stable, uint8_t* frozen,
+                                const float* mean_entropy, int G, int R, int stability, float conf_thr,
+                                int32_t* n_frozen, hipStream_t st) {
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(adaptive_stop_kernel, dim3(1), dim3(1024), 0, st, argmax, prev, stable, frozen, mean_entropy, G,
+                     R, stability, conf_thr, n_frozen);
   return hipGetLastError();
 }
 

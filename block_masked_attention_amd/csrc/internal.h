@@ -65,6 +65,14 @@ hipError_t bwd_launch(const BwdPlan& p, const void* q, const void* k, const void
                       const void* dout, const float* lse, void* dq, void* dk, void* dv, void* ws,
                       hipStream_t st);
 
+// Entropy-bound commit and adaptive stopping.
+hipError_t commit_entropy_launch(const CommitPlan& p, const void* logits, int64_t* tokens, uint8_t* masked,
+                                 float bound, float temperature, int k_min, void* ws, hipStream_t st);
+int commit_entropy_max_rows();
+hipError_t adaptive_stop_launch(const int64_t* argmax, int64_t* prev, int32_t* stable, uint8_t* frozen,
+                                const float* mean_entropy, int G, int R, int stability, float conf_thr,
+                                int32_t* n_frozen, hipStream_t st);
+
 // SPRINT prefix retention.
 int sprint_keep(int n, float r);
 size_t sprint_lds_bytes(int L);

@@ -189,6 +189,49 @@ int bda_verify_crop(const void* logits, int dtype, const int64_t* drafts, int64_
                     void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Entropy-bound commit ([DGemma] Schedulers: the entropy-bound scheduler
+ * commits the lowest-entropy positions whose joint entropy stays within a
+ * bound, so that roughly independent tokens are accepted together).
+ * logits [G, R, V] (BDA_BF16 or BDA_F32, finite); masked [G, R] uint8 and
+ * tokens [G, R] int64, updated in place as by bda_commit.  For every masked
+ * row: H = entropy in nats of softmax(logits / temperature), a = lowest index
+ * of the largest logit.  Per group, the masked rows ordered by (H ascending,
+ * row ascending) are committed (tokens = a, masked = 0) while the running sum
+ * of their H stays <= entropy_bound, and at least min(k_min, #masked) of them.
+ * The sum is the joint entropy of positions taken as independent; the
+ * scheduler's sampling and its temperature schedule are the caller's (pass
+ * the step's temperature).  temperature > 0 and finite, k_min >= 0,
+ * R <= 4096 (else BDA_EUNSUPPORTED).  Decisions are taken in fp32.
+ * workspace: at least bda_commit_entropy_workspace_bytes(G, R, V) bytes.
+ */
+int bda_commit_entropy(const void* logits, int dtype, int64_t* tokens, uint8_t* masked,
+                       float entropy_bound, float temperature, int k_min, int G, int R, int V,
+                       void* workspace, size_t ws_bytes, void* stream);
+size_t bda_commit_entropy_workspace_bytes(int G, int R, int V);
+
+/*
+ * One step of adaptive stopping ([DGemma] "Adaptive stopping": an example is
+ * frozen once its argmax predictions have been stable for stability_threshold
+ * steps and its mean per-token entropy is below the confidence threshold;
+ * the loop ends when every example is frozen).  Per example g of G (R
+ * positions each), on device arrays:
+ *   argmax [G, R] int64           this step's argmax (e.g. from bda_row_stats),
+ *   prev_argmax [G, R] int64      last step's (in/out; start with -1),
+ *   stable_steps [G] int32        consecutive unchanged steps (in/out; start 0),
+ *   frozen [G] uint8              in/out (start 0),
+ *   mean_entropy [G] float        this step's mean entropy (bda_row_stats).
+ * A frozen example keeps its state.  Otherwise stable_steps = (argmax ==
+ * prev_argmax at every position) ? stable_steps + 1 : 0, prev_argmax =
+ * argmax, and frozen = 1 once stable_steps >= stability_threshold and
+ * mean_entropy < confidence_threshold.  n_frozen (int32, device, may be NULL)
+ * receives the number of frozen examples after the step.  One kernel.
+ */
+int bda_adaptive_stop(const int64_t* argmax, int64_t* prev_argmax, int32_t* stable_steps,
+                      uint8_t* frozen, const float* mean_entropy, int G, int R,
+                      int stability_threshold, float confidence_threshold, int32_t* n_frozen,
+                      void* stream);
+
+/*
  * Per-row statistics of a softmax over the vocabulary, for adaptive stopping
  * and entropy-based commits ([DGemma] adaptive stopping: freeze an example
  * once its argmax is stable and its mean per-token entropy is below a

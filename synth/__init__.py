@@ -296,3 +296,22 @@ def varlen_case(seed: int, B: int, Hq: int, Hkv: int, d: int, n: int, cap: int):
     k = normal((B, Hkv, cap, d), 1.0, g)
     v = normal((B, Hkv, cap, d), 1.0, g)
     return q, k, v
+
+
+def spread_logits(seed: int, G: int, R: int, V: int, dtype=torch.bfloat16):
+    """Logits [G, R, V] whose rows range from nearly uniform to sharply
+    peaked: row noise N(0, sigma_r^2) with sigma_r ~ U(0.3, 4), then, in about
+    half the rows, one uniformly drawn index raised to the row's largest noise
+    value + U(0, 12).  Draw order: sigmas, noise, peak flags, indices, offsets."""
+    g = _gen(seed)
+    sig = 0.3 + 3.7 * torch.rand(G, R, 1, generator=g, dtype=torch.float32)
+    x = torch.randn(G, R, V, generator=g, dtype=torch.float32) * sig
+    flag = torch.rand(G, R, generator=g, dtype=torch.float32) < 0.5
+    idx = torch.randint(0, V, (G, R), generator=g, dtype=torch.int64)
+    off = 12.0 * torch.rand(G, R, generator=g, dtype=torch.float32)
+    x = x.to(dtype)
+    top = x.float().amax(dim=-1)
+    peak = (top + off).to(dtype)
+    cur = x.gather(-1, idx.unsqueeze(-1)).squeeze(-1)
+    x.scatter_(-1, idx.unsqueeze(-1), torch.where(flag, peak, cur).unsqueeze(-1))
+    return x

@@ -198,3 +198,27 @@ def test_varlen_cache_validation():
     assert c(A, 0, Bp, Cp, Dp, E, 0, 2, 28, 100, Wp, 1 << 20, None) == 1
     assert c(A, 0, Bp, Cp, Dp, ctypes.c_void_p((4 << 32) + 4), 100, 2, 28, 100, Wp, 1 << 20, None) == 1  # in accept
     assert c(A, 0, Bp, Cp, Dp, E, 100, 2, 28, 100, None, 0, None) == 3
+
+
+def test_entropy_commit_and_adaptive_stop_validation():
+    f = bda.lib.bda_commit_entropy
+    # logits, dtype, tokens, masked, bound, temperature, k_min, G, R, V, ws, ws_bytes, stream
+    need = bda.lib.bda_commit_entropy_workspace_bytes(2, 28, 1000)
+    assert need == bda.lib.bda_commit_workspace_bytes(2, 28, 1000)
+    assert f(A, 0, Bp, Cp, 1.0, 1.0, 1, 0, 28, 1000, None, 0, None) == 0            # nothing to do
+    assert f(A, 0, Bp, Cp, 1.0, 0.0, 1, 2, 28, 1000, Wp, need, None) == 1           # temperature
+    assert f(A, 0, Bp, Cp, 1.0, float("inf"), 1, 2, 28, 1000, Wp, need, None) == 1
+    assert f(A, 0, Bp, Cp, float("nan"), 1.0, 1, 2, 28, 1000, Wp, need, None) == 1
+    assert f(A, 0, Bp, Cp, 1.0, 1.0, -1, 2, 28, 1000, Wp, need, None) == 1          # k_min
+    assert f(A, 0, Bp, Cp, 1.0, 1.0, 1, 2, 4097, 1000, Wp, 1 << 30, None) == 2      # rows per group
+    assert f(A, 0, Bp, Cp, 1.0, 1.0, 1, 2, 28, 1000, Wp, need - 1, None) == 3
+    assert f(A, 0, None, Cp, 1.0, 1.0, 1, 2, 28, 1000, Wp, need, None) == 1
+    s = bda.lib.bda_adaptive_stop
+    # argmax, prev, stable, frozen, mean_entropy, G, R, stability, conf, n_frozen, stream
+    assert s(A, Bp, Cp, Dp, Wp, -1, 28, 1, 0.005, None, None) == 1
+    assert s(A, Bp, Cp, Dp, Wp, 2, 28, -1, 0.005, None, None) == 1
+    assert s(A, Bp, Cp, Dp, Wp, 2, 28, 1, float("nan"), None, None) == 1
+    assert s(A, None, Cp, Dp, Wp, 2, 28, 1, 0.005, None, None) == 1
+    assert s(ctypes.c_void_p((1 << 32) + 4), Bp, Cp, Dp, Wp, 2, 28, 1, 0.005, None, None) == 1   # misaligned
+    assert s(A, ctypes.c_void_p((1 << 32) + 64), Cp, Dp, Wp, 2, 28, 1, 0.005, None, None) == 1   # prev in argmax
+    assert s(A, Bp, Cp, Dp, Wp, 0, 28, 1, 0.005, None, None) == 0                   # nothing to do
