@@ -457,23 +457,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dka[dt] = dva[dt] = f32x16{};
 
-  auto compute = [&](int st) {
+  // Whether every slot of stage st sees every key of the wavefront (then no
+  // per-element mask is needed).  A block the wavefront cannot see at all
+  // gets P = dS = 0 from the per-slot thresholds.
+  const bool full_wave = wk1 - wk0 == 32;
+  auto seen_all = [&](int st) -> bool {
+    const int my_t = sthr[st][ql];
+    const bool lane_ok = clean ? my_t >= wb1 : (wb0 == wb1 && my_t == wb0);
+    return full_wave && __all(lane_ok);
+  };
+  // S^T-shaped scores and dP of the query block in stage st
+  auto sdp = [&](int st, f32x16& sv, f32x16& dp) {
     const uint16_t* qb = &qd[st][0];
     const uint16_t* db = &qd[st][QE];
-    // whole-block decision from the 32 slot thresholds (uniform per wave)
-    const int my_t = sthr[st][ql];
-    bool any_seen, all_seen;
-    if (wk1 <= wk0) {
-      any_seen = all_seen = false;
-    } else if (clean) {
-      any_seen = __any(my_t >= wb0);
-      all_seen = __all(my_t >= wb1) && wk1 - wk0 == 32;
-    } else {
-      any_seen = __any(my_t >= wb0 && my_t <= wb1);
-      all_seen = wb0 == wb1 && __all(my_t == wb0) && wk1 - wk0 == 32;
-    }
-    if (!any_seen) return;
-    f32x16 sv{}, dp{};
+    sv = f32x16{};
+    dp = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       const bf16x8 qa = *(const bf16x8*)(qb + ql * D + 8 * ((2 * ks + hb) ^ q_swz));
@@ -481,6 +479,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
       sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kop[ks], sv, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vop[ks], dp, 0, 0, 0);
     }
+  };
+  // P, dS and the dV, dK updates of the query block in stage st
+  auto grads = [&](int st, const f32x16& sv, const f32x16& dp, bool all_seen) {
+    const uint16_t* qb = &qd[st][0];
+    const uint16_t* db = &qd[st][QE];
     // lane = key (column), value i = slot 8*(i/4) + 4*hb + (i%4)
     f32x4 l4[4], d4[4];
     i32x4 t4[4];
@@ -539,11 +542,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
       kop[ks] = *(const bf16x8*)(kv + kr_off + 8 * ((2 * ks + hb) ^ k_swz));
       vop[ks] = *(const bf16x8*)(kv + KE + kr_off + 8 * ((2 * ks + hb) ^ k_swz));
     }
+    // Software-pipelined over query blocks: the S and dP MFMAs of block t + 1
+    // are issued with the P / dS arithmetic and the dV / dK MFMAs of block t
+    // (one wavefront per SIMD, so the overlap has to come from within it).
+    // Block t + 1 is visible here: the settle of the previous step left only
+    // the newest block (t + 2) in flight.
+    f32x16 sv0, dp0, sv1, dp1;
+    sdp(0, sv0, dp0);
+    bool all0 = seen_all(0);
 #pragma unroll 1
     for (int t = 0; t < nblk; ++t) {
-      issue(t + 3, (t + 3) % NS);
-      compute(t % NS);
+      sdp((t + 1) % NS, sv1, dp1);             // past the last block: stale data, never used
+      grads(t % NS, sv0, dp0, all0);
+      const bool all1 = seen_all((t + 1) % NS);
+      issue(t + 3, (t + 3) % NS);              // into the stage of block t - 1, free since the last barrier
       settle();
+      sv0 = sv1;
+      dp0 = dp1;
+      all0 = all1;
     }
   }
   drain();
