@@ -9,13 +9,15 @@
 // sec. 2 of the Nemotron-Labs-Diffusion-8B-Base 3x analysis page).
 //
 // Pass 1 (stream): one workgroup per (row, vocabulary chunk) streams the
-// logits once with 16-byte non-temporal loads and keeps, per lane, the
-// running maximum m, the lowest index a reaching it and Z = sum exp(l - m)
-// (rescaled when m grows).  Lanes and wavefronts merge with the associative
-// rule  m = max(m1, m2);  Z = Z1 e^(m1-m) + Z2 e^(m2-m);  a = lowest index
-// among the maxima, in a fixed order, so results do not depend on timing.
+// logits once with 16-byte non-temporal loads into registers, takes the
+// chunk's maximum m (wavefront and workgroup reductions), then Z = sum
+// exp(l - m) against it; only the threads holding m look for its lowest
+// index a.  A ragged chunk instead keeps a running (m, a, Z) per lane,
+// rescaled when m grows.  Partials merge with the associative rule
+// m = max(m1, m2);  Z = Z1 e^(m1-m) + Z2 e^(m2-m);  a = lowest index among
+// the maxima, in a fixed order, so results do not depend on timing.
 // Pass 2 (finalize): one workgroup per group merges the chunk partials of
-// its rows in chunk order, takes p = 1/Z, applies the threshold and the
+// its rows in a fixed tree, takes p = 1/Z, applies the threshold and the
 // minimum-count fallback, and writes tokens / masked.
 //
 // Row statistics (entropy for adaptive stopping and entropy-bound commits,
@@ -65,6 +67,32 @@ __device__ __forceinline__ Stat merge(Stat x, Stat y, int kind, float c = kLog2e
       r.t = (x.m == -INFINITY ? 0.f : ax * (x.t + dx * x.z)) + (y.m == -INFINITY ? 0.f : ay * (y.t + dy * y.z));
   }
   return r;
+}
+
+// Largest of two finite values (v_maximum3_f32: no quieting of the inputs,
+// which fmaxf adds for values built from raw bits).
+__device__ __forceinline__ float vmax(float x, float y) { return __builtin_elementwise_maximum(x, y); }
+
+// All-lane reductions of a wavefront without LDS: DPP within rows of 16
+// (lanes i^1, i^2, the mirror within 8, the mirror within 16), then the row
+// swap and the half swap.  Every step combines a lane with its partner in an
+// order both lanes share, so every lane ends with the same value.
+template <int CTRL>
+__device__ __forceinline__ int dpp(int x) {
+  return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xF, 0xF, false);
+}
+template <typename T, typename F>
+__device__ __forceinline__ T wave_all(T x, F op) {
+  auto as_i = [](T v) { return __builtin_bit_cast(int, v); };
+  auto as_t = [](int v) { return __builtin_bit_cast(T, v); };
+  x = op(x, as_t(dpp<0xB1>(as_i(x))));
+  x = op(x, as_t(dpp<0x4E>(as_i(x))));
+  x = op(x, as_t(dpp<0x141>(as_i(x))));
+  x = op(x, as_t(dpp<0x140>(as_i(x))));
+  auto r = __builtin_amdgcn_permlane16_swap((unsigned)as_i(x), (unsigned)as_i(x), false, false);
+  x = op(as_t((int)r[0]), as_t((int)r[1]));
+  auto h = __builtin_amdgcn_permlane32_swap((unsigned)as_i(x), (unsigned)as_i(x), false, false);
+  return op(as_t((int)h[0]), as_t((int)h[1]));
 }
 
 template <bool BF16>
@@ -157,23 +185,43 @@ __global__ __launch_bounds__(kCommitThreads) void stream_kernel(const void* __re
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[v][e] = w[v][e >> 2][e & 3];
     }
-    // pass 1: largest value and its lowest index
+    // pass 1: the chunk's largest value M, known to every thread
+    const int lane = tid & 63, wv = tid >> 6;
+    float vm[VPT];
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
-      float lm = x[v][0];
+      vm[v] = x[v][0];
 #pragma unroll
-      for (int e = 1; e < 8; ++e) lm = fmaxf(lm, x[v][e]);
-      if (lm > s.m) {
-        int idx = 7;
-#pragma unroll
-        for (int e = 6; e >= 0; --e) idx = x[v][e] == lm ? e : idx;
-        s.m = lm;
-        s.a = c0 + 8 * (v * kCommitThreads + tid) + idx;
-      }
+      for (int e = 1; e < 8; ++e) vm[v] = vmax(vm[v], x[v][e]);
     }
-    // pass 2: Z (and T) against that maximum
+    float tm = vm[0];
+#pragma unroll
+    for (int v = 1; v < VPT; ++v) tm = vmax(tm, vm[v]);
+    __shared__ float wmax[kCommitThreads / 64];
+    __shared__ int wa[kCommitThreads / 64];
+    __shared__ float wz[kCommitThreads / 64], wt[kCommitThreads / 64];
+    const float wm = wave_all(tm, vmax);
+    if (lane == 0) wmax[wv] = wm;
+    __syncthreads();
+    float M = wmax[0];
+#pragma unroll
+    for (int w = 1; w < kCommitThreads / 64; ++w) M = vmax(M, wmax[w]);
+    // lowest index holding M: only the threads that hold it search
+    int a = INT_MAX;
+    if (tm == M) {
+#pragma unroll
+      for (int v = VPT - 1; v >= 0; --v)
+        if (vm[v] == M) {
+          int idx = 7;
+#pragma unroll
+          for (int e = 6; e >= 0; --e) idx = x[v][e] == M ? e : idx;
+          a = c0 + 8 * (v * kCommitThreads + tid) + idx;
+        }
+    }
+    // pass 2: Z (and T) against M; every thread's sums share it, so they add
+    float z = 0.f, tt = 0.f;
     if (KIND != kArgmax) {
-      const float nb = -s.m * xs;
+      const float nb = -M * xs;
       float acc[4] = {0.f, 0.f, 0.f, 0.f}, acct[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int v = 0; v < VPT; ++v)
@@ -181,11 +229,30 @@ __global__ __launch_bounds__(kCommitThreads) void stream_kernel(const void* __re
         for (int e = 0; e < 8; ++e) {
           const float p = exp2_fast(fmaf(x[v][e], xs, nb));
           acc[e & 3] += p;
-          if (KIND == kWithZT) acct[e & 3] = fmaf(p, x[v][e] - s.m, acct[e & 3]);
+          if (KIND == kWithZT) acct[e & 3] = fmaf(p, x[v][e] - M, acct[e & 3]);
         }
-      s.z = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-      s.t = (acct[0] + acct[1]) + (acct[2] + acct[3]);
+      z = wave_all((acc[0] + acc[1]) + (acc[2] + acc[3]), [](float u, float w) { return u + w; });
+      if (KIND == kWithZT)
+        tt = wave_all((acct[0] + acct[1]) + (acct[2] + acct[3]), [](float u, float w) { return u + w; });
     }
+    a = wave_all(a, [](int u, int w) { return min(u, w); });
+    if (lane == 0) {
+      wa[wv] = a;
+      wz[wv] = z;
+      wt[wv] = tt;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      Partial p{M, wz[0], wa[0], wt[0]};
+#pragma unroll
+      for (int w = 1; w < kCommitThreads / 64; ++w) {
+        p.a = min(p.a, wa[w]);
+        p.z += wz[w];
+        p.t += wt[w];
+      }
+      part[(size_t)t * n_chunks + c] = p;
+    }
+    return;
   } else if (vec_ok) {
     // 8 consecutive values per step: one 16-byte load (bf16) or two (fp32).
     for (int base = c0 + 8 * tid; base < c1; base += 8 * kCommitThreads) {
@@ -249,13 +316,31 @@ __global__ __launch_bounds__(kCommitThreads) void stream_kernel(const void* __re
   }
 }
 
-__device__ __forceinline__ Stat row_stat(const Partial* part, size_t t, int n_chunks, int kind,
-                                        float c = kLog2e) {
-  const Partial& q0 = part[t * n_chunks];
-  Stat s{q0.m, q0.z, q0.a, q0.t};
-  for (int ci = 1; ci < n_chunks; ++ci) {
-    const Partial& q = part[t * n_chunks + ci];
-    s = merge(s, Stat{q.m, q.z, q.a, q.t}, kind, c);
+// Rows of a finalize workgroup are merged by groups of CH lanes (CH = the
+// power of two >= the chunk count, at most 64): lane ci of a row loads the
+// partials of chunks ci, ci + CH, ... at once, then the lanes merge in a
+// fixed tree, every lane of the row ending with the row's Stat.  live must be
+// the same in all CH lanes of a row.
+__device__ __forceinline__ int lanes_per_row(int n_chunks) {
+  int ch = 1;
+  while (ch < n_chunks && ch < 64) ch <<= 1;
+  return ch;
+}
+__device__ __forceinline__ Stat row_stat_lanes(const Partial* part, size_t t, bool live, int ci, int CH,
+                                              int n_chunks, int kind, float c = kLog2e) {
+  Stat s{-INFINITY, 0.f, INT_MAX, 0.f};
+  if (live)
+    for (int k = ci; k < n_chunks; k += CH) {
+      const Partial q = part[t * n_chunks + k];
+      s = merge(s, Stat{q.m, q.z, q.a, q.t}, kind, c);
+    }
+  for (int off = 1; off < CH; off <<= 1) {
+    Stat o;
+    o.m = __shfl_xor(s.m, off);
+    o.z = __shfl_xor(s.z, off);
+    o.a = __shfl_xor(s.a, off);
+    o.t = __shfl_xor(s.t, off);
+    s = merge(s, o, kind, c);
   }
   return s;
 }
@@ -272,51 +357,79 @@ __device__ __forceinline__ int block_sum(int x, int* red) {
   return s;
 }
 
-// One workgroup per group g.  rowp/rowa/rowf are workspace scratch [G*R].
+// One workgroup per group g.  Row results (p, argmax, flag) live in LDS
+// when R <= kFinRows, else in the workspace scratch rowp/rowa/rowf [G*R].
+// Each row's mask byte and chunk partials are loaded together (partials of
+// unmasked rows are stale and ignored), so the critical path holds one
+// round trip to memory.
+constexpr int kFinRows = 2048;
+
+template <bool IN_LDS>
 __global__ __launch_bounds__(kCommitThreads) void commit_finalize_kernel(
     const Partial* __restrict__ part, int n_chunks, int64_t* __restrict__ tokens,
     uint8_t* __restrict__ masked, float threshold, int k_min, int R, float* __restrict__ rowp,
     int* __restrict__ rowa, uint8_t* __restrict__ rowf) {
-  __shared__ int red[kCommitThreads / 64];
-  const int g = blockIdx.x;
+  __shared__ int red[2][kCommitThreads / 64];
+  __shared__ float lp[IN_LDS ? kFinRows : 1];
+  __shared__ int la[IN_LDS ? kFinRows : 1];
+  __shared__ uint8_t lf[IN_LDS ? kFinRows : 1];
+  const int g = blockIdx.x, tid = threadIdx.x;
   const size_t base = (size_t)g * R;
+  float* rp = IN_LDS ? lp : rowp + base;
+  int* ra = IN_LDS ? la : rowa + base;
+  uint8_t* rf = IN_LDS ? lf : rowf + base;
   int nmask = 0, npass = 0;
-  for (int r = threadIdx.x; r < R; r += kCommitThreads) {
-    const size_t t = base + r;
-    uint8_t f = 0;
-    if (masked[t]) {
-      const Stat s = row_stat(part, t, n_chunks, kWithZ);
+  const int CH = lanes_per_row(n_chunks), ci = tid % CH;
+  for (int r0 = 0; r0 < R; r0 += kCommitThreads / CH) {
+    const int r = r0 + tid / CH;
+    const bool in = r < R;
+    const uint8_t mk = in && ci == 0 ? masked[base + r] : 0;
+    const Stat s = row_stat_lanes(part, base + r, in, ci, CH, n_chunks, kWithZ);
+    if (in && ci == 0) {
       const float p = 1.f / s.z;
-      rowp[t] = p;
-      rowa[t] = s.a;
-      f = p > threshold ? 2 : 1;
-      nmask += 1;
+      const uint8_t f = mk ? (p > threshold ? 2 : 1) : 0;
+      rp[r] = p;
+      ra[r] = s.a;
+      rf[r] = f;
+      nmask += f != 0;
       npass += f == 2;
     }
-    rowf[t] = f;
   }
-  nmask = block_sum(nmask, red);
-  npass = block_sum(npass, red);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    nmask += __shfl_xor(nmask, off);
+    npass += __shfl_xor(npass, off);
+  }
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = nmask;
+    red[1][tid >> 6] = npass;
+  }
+  __syncthreads();   // also publishes rp, ra, rf
+  nmask = 0;
+  npass = 0;
+#pragma unroll
+  for (int w = 0; w < kCommitThreads / 64; ++w) {
+    nmask += red[0][w];
+    npass += red[1][w];
+  }
   const int need = min(k_min, nmask) - npass;
-  __syncthreads();
-  for (int r = threadIdx.x; r < R; r += kCommitThreads) {
-    const size_t t = base + r;
-    const uint8_t f = rowf[t];
+  for (int r = tid; r < R; r += kCommitThreads) {
+    const uint8_t f = rf[r];
     bool take = f == 2;
     if (f == 1 && need > 0) {
       // rank among masked rows below the threshold: larger p first, then lower row
-      const float p = rowp[t];
+      const float p = rp[r];
       int rank = 0;
       for (int o = 0; o < R && rank < need; ++o) {
-        if (rowf[base + o] != 1) continue;
-        const float po = rowp[base + o];
+        if (rf[o] != 1) continue;
+        const float po = rp[o];
         rank += (po > p) || (po == p && o < r);
       }
       take = rank < need;
     }
     if (take) {
-      tokens[t] = rowa[t];
-      masked[t] = 0;
+      tokens[base + r] = ra[r];
+      masked[base + r] = 0;
     }
   }
 }
@@ -329,11 +442,16 @@ __global__ __launch_bounds__(kCommitThreads) void verify_finalize_kernel(
   __shared__ int red[kCommitThreads / 64];
   const int b = blockIdx.x;
   int first = R;
-  for (int r = threadIdx.x; r < R; r += kCommitThreads) {
+  const int CH = lanes_per_row(n_chunks), ci = threadIdx.x % CH;
+  for (int r0 = 0; r0 < R; r0 += kCommitThreads / CH) {
+    const int r = r0 + (int)threadIdx.x / CH;
     const size_t t = (size_t)b * R + r;
-    const Stat s = row_stat(part, t, n_chunks, kArgmax);
-    argmax_out[t] = s.a;
-    if ((int64_t)s.a != drafts[t]) first = min(first, r);
+    const int64_t dr = r < R && ci == 0 ? drafts[t] : 0;
+    const Stat s = row_stat_lanes(part, t, r < R, ci, CH, n_chunks, kArgmax);
+    if (r < R && ci == 0) {
+      argmax_out[t] = s.a;
+      if ((int64_t)s.a != dr) first = min(first, r);
+    }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) first = min(first, __shfl_xor(first, off));
@@ -371,10 +489,13 @@ __global__ __launch_bounds__(kCommitThreads) void stats_finalize_kernel(
   const int g = blockIdx.x;
   float hsum = 0.f;
   int cnt = 0;
-  for (int r = threadIdx.x; r < R; r += kCommitThreads) {
+  const int CH = lanes_per_row(n_chunks), ci = threadIdx.x % CH;
+  for (int r0 = 0; r0 < R; r0 += kCommitThreads / CH) {
+    const int r = r0 + (int)threadIdx.x / CH;
     const size_t t = (size_t)g * R + r;
-    if (masked != nullptr && masked[t] == 0) continue;
-    const Stat s = row_stat(part, t, n_chunks, kWithZT);
+    const bool live = r < R && ci == 0 && (masked == nullptr || masked[t] != 0);
+    const Stat s = row_stat_lanes(part, t, r < R, ci, CH, n_chunks, kWithZT);   // stale for unselected rows
+    if (!live) continue;
     const float h = logf(s.z) - s.t / s.z;
     if (conf) conf[t] = 1.f / s.z;
     if (argmax_out) argmax_out[t] = s.a;
@@ -408,11 +529,15 @@ __global__ __launch_bounds__(kCommitThreads) void commit_entropy_finalize_kernel
   const int g = blockIdx.x, tid = threadIdx.x;
   const size_t base = (size_t)g * R;
   int nm = 0;
-  for (int r = tid; r < R; r += kCommitThreads) {
+  const int CH = lanes_per_row(n_chunks), ci = tid % CH;
+  for (int r0 = 0; r0 < R; r0 += kCommitThreads / CH) {
+    const int r = r0 + tid / CH;
+    const bool live = r < R && ci == 0 && masked[base + r];
+    const Stat st = row_stat_lanes(part, base + r, r < R, ci, CH, n_chunks, kWithZT, c);   // stale for unmasked rows
+    if (r >= R || ci != 0) continue;
     float h = INFINITY;                          // unmasked: never ranked
     int a = -1;
-    if (masked[base + r]) {
-      const Stat st = row_stat(part, base + r, n_chunks, kWithZT, c);
+    if (live) {
       h = logf(st.z) - (st.t * inv_t) / st.z;
       a = st.a;
       nm += 1;
@@ -568,8 +693,12 @@ hipError_t commit_launch(const CommitPlan& p, const void* logits, int64_t* token
   (void)hipGetLastError();
   hipError_t e = launch_stream<kWithZ>(p, logits, masked, part, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(commit_finalize_kernel, dim3(p.G), dim3(kCommitThreads), 0, st, part,
-                     p.n_chunks, tokens, masked, threshold, k_min, p.R, rowp, rowa, rowf);
+  if (p.R <= kFinRows)
+    hipLaunchKernelGGL(commit_finalize_kernel<true>, dim3(p.G), dim3(kCommitThreads), 0, st, part,
+                       p.n_chunks, tokens, masked, threshold, k_min, p.R, rowp, rowa, rowf);
+  else
+    hipLaunchKernelGGL(commit_finalize_kernel<false>, dim3(p.G), dim3(kCommitThreads), 0, st, part,
+                       p.n_chunks, tokens, masked, threshold, k_min, p.R, rowp, rowa, rowf);
   return hipGetLastError();
 }
 

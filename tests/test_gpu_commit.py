@@ -83,6 +83,7 @@ def _uniform(G, R, V, seed, dtype, scale=2.0):
     (1, 7, 1, torch.bfloat16, 0.5, 0),         # V = 1: p = 1 everywhere
     (4, 40, 20000, torch.float32, 0.99, 5),    # two vocabulary chunks, fallback only
     (2, 300, 64, torch.bfloat16, 0.2, 3),      # R above the finalize block size
+    (2, 2100, 64, torch.bfloat16, 0.2, 3),     # R above the rows the finalize keeps in LDS
     (2, 9, 4096, torch.bfloat16, 0.0, 0),      # tau = 0: every masked row passes
     (2, 9, 4096, torch.bfloat16, 1.0, 100),    # nothing passes, k_min > #masked
 ])
