@@ -227,13 +227,14 @@ __global__ __launch_bounds__(kCommitThreads) void stream_kernel(const void* __re
       for (int v = 0; v < VPT; ++v)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float p = exp2_fast(fmaf(x[v][e], xs, nb));
+          const float u = fmaf(x[v][e], xs, nb);   // (l - M) xs
+          const float p = exp2_fast(u);
           acc[e & 3] += p;
-          if (KIND == kWithZT) acct[e & 3] = fmaf(p, x[v][e] - M, acct[e & 3]);
+          if (KIND == kWithZT) acct[e & 3] = fmaf(p, u, acct[e & 3]);
         }
       z = wave_all((acc[0] + acc[1]) + (acc[2] + acc[3]), [](float u, float w) { return u + w; });
-      if (KIND == kWithZT)
-        tt = wave_all((acct[0] + acct[1]) + (acct[2] + acct[3]), [](float u, float w) { return u + w; });
+      if (KIND == kWithZT)   // T = sum p (l - M) = (sum p u) / xs
+        tt = wave_all((acct[0] + acct[1]) + (acct[2] + acct[3]), [](float u, float w) { return u + w; }) / xs;
     }
     a = wave_all(a, [](int u, int w) { return min(u, w); });
     if (lane == 0) {
