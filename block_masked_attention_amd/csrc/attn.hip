@@ -610,6 +610,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       const int idx = item_of(r);
       if (idx < 0) break;
       begin_item(idx);
+      // The Q operands land here, once per item.  Left to the compiler, the
+      // wait for them sits at their first use inside the tile loop, where
+      // vmcnt(0) would also wait for the DMA loads just issued three tiles
+      // ahead (the counter retires in order and counts those loads too).
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (0xF << 8));   // vmcnt(0) only
       reset_acc();
       const int nf = cur.nf, nt = cur.nt;
       if (nt > 0) {
