@@ -81,6 +81,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
   const int w = tid >> 6;
   const int ql = lane & 31;
   const int hb = lane >> 5;
+  // STAGES = 5 (DECODE/CAUSAL): the wavefronts form two groups over the same
+  // query slots; group kg computes the 32-key half kg of every staged tile.
+  constexpr bool KS = STAGES == 5;
+  constexpr int NWQ = KS ? NW / 2 : NW;       // wavefronts per group of query slots
+  const int kg = KS ? w / NWQ : 0;
+  const int wq = KS ? w - kg * NWQ : w;
 
   // ---- work items.  The canonical order (index -> batch, kv head, query
   // tile, key split) hands out the heaviest query tiles first.  With
@@ -127,6 +133,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       const int nfull = full_hi > lo ? (full_hi - lo) / kBN : 0;
       F = Span{lo, lo + nfull * kBN};
       R1 = Span{F.hi, imax(F.hi, hi)};
+    }
+    // The persistent walk needs a boundary tile at the end of every item (its
+    // ring wait relies on it); an item of full tiles only gives up its last.
+    if (STAGES == 4 && R1.hi <= R1.lo && R2.hi <= R2.lo && F.hi > F.lo) {
+      F.hi -= kBN;
+      R1 = Span{F.hi, F.hi + kBN};
     }
     gm.F = F;
     gm.R1 = R1;
@@ -180,7 +192,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
         qrow[qb] = half * a.L + pos;
         head[qb] = g * a.G + (s - rloc * a.G);
       } else {
-        const int s = (w * NQB + qb) * 32 + ql;
+        const int s = (wq * NQB + qb) * 32 + ql;
         const int rloc = s / a.G;
         const int r = cur.qt * a.rows_per_wg + rloc;
         valid[qb] = rloc < a.rows_per_wg && r < a.n;
@@ -397,11 +409,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
   // contiguous 1 KB run, so the lane picks the global chunk that the
   // permuted layout puts there.
   constexpr int DJ = TCH >= NT ? TCH / NT : 1;   // DMA loads per wavefront per matrix
-  auto dma = [&](const Geom& gm, int j, uint16_t* st) {
-    int t0, t1;
-    tile_in(gm, j, t0, t1);
-    const uint16_t* kb = a.k + (size_t)gm.pair * a.Sk * D;
-    const uint16_t* vb = a.v + (size_t)gm.pair * a.Sk * D;
+  auto dma_keys = [&](int pair, int t0, int t1, uint16_t* st) {
+    const uint16_t* kb = a.k + (size_t)pair * a.Sk * D;
+    const uint16_t* vb = a.v + (size_t)pair * a.Sk * D;
 #pragma unroll
     for (int q = 0; q < DJ; ++q) {
       const int run = w * DJ + q;                 // 64-chunk run of the tile
@@ -415,6 +425,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
         lds_dma16(vb + off, dst + TE);
       }
     }
+  };
+  auto dma = [&](const Geom& gm, int j, uint16_t* st) {
+    int t0, t1;
+    tile_in(gm, j, t0, t1);
+    dma_keys(gm.pair, t0, t1, st);
   };
   // All but the newest tile's DMA loads (and every LDS access) have landed;
   // then the workgroup barrier (without the fence of __syncthreads, which
@@ -447,7 +462,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       if (valid[qb]) row_spans(a.mode, VARLEN ? cur.L : a.L, a.n, a.blk, qrow[qb], A[qb], C[qb]);
     }
 #pragma unroll 1
-    for (int sub = 0; sub < 2; ++sub) {
+    for (int sub = KS ? kg : 0; sub < (KS ? kg + 1 : 2); ++sub) {
       const int e0 = t0 + 32 * sub, e1 = imin(t1, e0 + 32);
       if (e0 >= e1) break;
       bool full = true, empty = true;
@@ -560,6 +575,87 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       }
     }
     finish();
+  } else if constexpr (KS) {
+    // ---- DECODE/CAUSAL, one item per workgroup.  A 5-stage DMA ring keeps
+    // up to four 64-key tiles in flight; wavefront group kg computes the
+    // 32-key half kg of every tile for all the item's query slots, and the
+    // two groups merge their (max, sum, O) through LDS at the end.
+    begin_item(blockIdx.x);
+    reset_acc();
+    const int nf = cur.nf, nt = cur.nt;
+    auto stq = [&](int j) { return smem + (j % STAGES) * STAGE; };
+    // Tile j visible to every wavefront, given that tiles 0 .. issued-1 have
+    // been issued: the (up to three) tiles issued after j stay in flight.
+    auto settle_for = [&](int j, int issued) {
+      const int newer = imin(STAGES - 2, imax(0, issued - 1 - j));
+      constexpr int T = 2 * DJ;                // DMA loads of one tile per wavefront
+      asm volatile("" ::: "memory");
+      if (newer >= 3)
+        __builtin_amdgcn_s_waitcnt(((3 * T) & 15) | (7 << 4) | (((3 * T) >> 4) << 14));
+      else if (newer == 2)
+        __builtin_amdgcn_s_waitcnt(((2 * T) & 15) | (7 << 4) | (((2 * T) >> 4) << 14));
+      else if (newer == 1)
+        __builtin_amdgcn_s_waitcnt((T & 15) | (7 << 4) | ((T >> 4) << 14));
+      else
+        __builtin_amdgcn_s_waitcnt(7 << 4);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    int issued = 0;
+    for (; issued < STAGES - 1 && issued < nt; ++issued) dma(cur, issued, stq(issued));
+    drain();   // the Q operands and the first tiles
+    // Tile i + 4 goes into the stage of tile i - 1, which every wavefront
+    // finished before the last barrier.
+#pragma unroll 1
+    for (int i = 0; i < nf; ++i) {
+      if (issued < nt) dma(cur, issued, stq(issued)), ++issued;
+      f32x16 sc[NQB];
+      bf16x8 pb[NQB][2];
+      qk_sub(stq(i), kg, sc);
+      softmax_fast(sc, pb);
+      pv_sub(stq(i), kg, pb);
+      settle_for(i + 1, issued);
+    }
+#pragma unroll 1
+    for (int i = nf; i < nt; ++i) {
+      if (issued < nt) dma(cur, issued, stq(issued)), ++issued;
+      slow_tile(stq(i), i);
+      settle_for(i + 1, issued);
+    }
+    drain();
+    // group 1 hands its state to group 0 through the (drained) ring
+    float* xf = reinterpret_cast<float*>(smem);
+    constexpr int NE = DT * 16 + 2;
+    auto xi = [&](int qb, int e) { return ((wq * NQB + qb) * NE + e) * 64 + lane; };
+    static_assert(NWQ * NQB * NE * 64 * 4 <= STAGES * STAGE * 2, "merge buffer exceeds the ring");
+    if (kg == 1) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) xf[xi(qb, dt * 16 + i)] = o[qb][dt][i];
+        xf[xi(qb, DT * 16)] = m_run[qb];
+        xf[xi(qb, DT * 16 + 1)] = l_run[qb];
+      }
+    }
+    __syncthreads();
+    if (kg == 0) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const float mb = xf[xi(qb, DT * 16)], lb = xf[xi(qb, DT * 16 + 1)];
+        const float M = fmaxf(m_run[qb], mb);
+        const float fa = m_run[qb] == -INFINITY ? 0.f : exp2_fast((m_run[qb] - M) * sl2);
+        const float fb = mb == -INFINITY ? 0.f : exp2_fast((mb - M) * sl2);
+        l_run[qb] = l_run[qb] * fa + lb * fb;
+        m_run[qb] = M;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[qb][dt][i] = o[qb][dt][i] * fa + xf[xi(qb, dt * 16 + i)] * fb;
+      }
+      finish();
+    }
   } else {
     // ---- persistent DMA-fed walk.  The workgroup takes items round by
     // round, in snake order (within its XCD when pairs_per_xcd > 0), so
@@ -594,10 +690,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       }
     };
     c_next_item();
-    auto c_issue = [&](uint16_t* st) {
-      if (!c_live) return;
+    // Returns whether a tile was issued.  The wait at the end of a tile step
+    // leaves only the newest tile in flight, so the tile the next step reads
+    // must not be the newest: every item ends with a boundary tile (see the
+    // geometry), fast steps are always followed by at least one more issued
+    // tile, and a boundary step that finds the stream exhausted waits for
+    // every load before it reads its tile.
+    auto c_issue = [&](uint16_t* st) -> bool {
+      if (!c_live) return false;
       dma(cg, c_j, st);
       if (++c_j == cg.nt) c_next_item();
+      return true;
     };
     int sp = 0;   // stream position of the current item's first tile
     auto stg = [&](int i) { return smem + ((sp + i) & 3) * STAGE; };
@@ -642,7 +745,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
         }
 #pragma unroll 1
         for (int i = nf; i < nt; ++i) {
-          c_issue(stg(i + 3));
+          if (!c_issue(stg(i + 3))) drain();
           slow_tile(stg(i), i);
           settle();
         }
@@ -741,21 +844,24 @@ int attn_make_plan(int B, int Hq, int Hkv, int L, int d, int block, int mode, At
     x.n = block;
     x.Sq = block;
     x.Sk = L;
-    x.nw = block >= 128 ? 8 : 4;
-    x.stages = block >= 128 ? 4 : 2;
+    // short query blocks over long caches (decode, verify): the split-key
+    // ring (one 8-wavefront workgroup per item, two groups of 4 over the
+    // same slots); long query ranges (prefill): the persistent walk
+    x.nw = 8;
+    x.stages = block >= 128 ? 4 : 5;
     x.qpw = 32;
-    const int slots = x.nw * x.qpw;
+    const int slots = (x.stages == 5 ? x.nw / 2 : x.nw) * x.qpw;
     if (x.G > slots) {
       *why = "Hq/Hkv larger than the query slots of a workgroup";
       return 2;
     }
     x.rows_per_wg = slots / x.G;
     x.n_qtiles = (block + x.rows_per_wg - 1) / x.rows_per_wg;
-    // Split the keys when (batch x kv head x query tile) alone cannot keep
-    // every CU streaming (two resident 4-wave workgroups per CU); each split
-    // keeps at least 4 key tiles.
+    // Split the keys when (batch x kv head x query tile) alone cannot give
+    // every CU a workgroup (one resident split-key workgroup per CU at
+    // d = 128, 256 CUs); each split keeps at least 4 key tiles.
     const long long items = (long long)B * Hkv * x.n_qtiles;
-    const long long target = 512;
+    const long long target = x.stages == 5 ? 256 : 512;
     int splits = (int)((target + items - 1) / items);
     const int max_splits = (L + 4 * kBN - 1) / (4 * kBN);
     if (splits > max_splits) splits = max_splits;
@@ -820,6 +926,8 @@ static hipError_t launch_d(const AttnPlan& p, AttnArgs a, hipStream_t st) {
     long long grid = p.grid < slots ? p.grid : slots;
     if (a.pairs_per_xcd > 0 && grid % 8 != 0) a.pairs_per_xcd = 0;
     e = launch_main<D, 8, 32, 4>(a, grid, st);
+  } else if (p.stages == 5) {
+    e = launch_main<D, 8, 32, 5>(a, p.grid, st);
   } else {
     e = launch_main<D, 4, 32, 2>(a, p.grid, st);
   }

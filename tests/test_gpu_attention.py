@@ -55,6 +55,9 @@ SMALL = [
     ("causal", 1, 8, 2, 300, 128, 300),    # prefill (n = L)
     ("causal", 2, 4, 1, 700, 64, 150),
     ("causal", 1, 2, 1, 65, 32, 1),
+    ("decode", 1, 8, 2, 512, 128, 128),    # 8-wave persistent walk, items of full tiles only
+    ("causal", 1, 8, 2, 256, 128, 129),    # last query tile (one row) sees all 256 keys
+    ("decode", 1, 4, 1, 20, 128, 20),      # fewer keys than half a tile: one key group sees none
 ]
 
 
