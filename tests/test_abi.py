@@ -57,9 +57,11 @@ def test_attn_validation(kw, code):
 
 def test_attn_workspace_sizes():
     assert bda.attn_workspace_bytes(4, 32, 8, 2048, 128, 32, "hybrid") == 0
-    need = bda.attn_workspace_bytes(32, 32, 8, 4124, 128, 28, "decode")
-    assert need > 0
-    assert _attn(mode=1, L=4124, block=28, Hq=32, Hkv=8, B=32, ws=Wp, nbytes=need - 1) == 3
+    # 32 x 8 (batch, kv head) items give every CU one: no key split
+    assert bda.attn_workspace_bytes(32, 32, 8, 4124, 128, 28, "decode") == 0
+    need = bda.attn_workspace_bytes(16, 32, 8, 8220, 128, 28, "causal")   # 128 items: two splits
+    assert need == 2 * 16 * 32 * 28 * (128 * 4 + 8)
+    assert _attn(mode=2, L=8220, block=28, Hq=32, Hkv=8, B=16, ws=Wp, nbytes=need - 1) == 3
     assert bda.attn_workspace_bytes(1, 3, 2, 10, 128, 2, "hybrid") == 0     # invalid -> 0
 
 
