@@ -421,8 +421,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
         const int c = pc ^ (swz<D>(r) & (CPR - 1));
         const size_t off = (size_t)imin(t0 + r, t1 - 1) * D + 8 * c;
         const uint16_t* dst = st + run * 64 * 8;
-        lds_dma16(kb + off, dst);
-        lds_dma16(vb + off, dst + TE);
+        if constexpr (KS) {   // each key is read once per item
+          lds_dma16_nt(kb + off, dst);
+          lds_dma16_nt(vb + off, dst + TE);
+        } else {
+          lds_dma16(kb + off, dst);
+          lds_dma16(vb + off, dst + TE);
+        }
       }
     }
   };

@@ -45,6 +45,11 @@ __device__ __forceinline__ void lds_dma16(const uint16_t* g, const uint16_t* lds
   const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_run);
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(base) : "memory");
 }
+// The same with the non-temporal hint, for data read once (streamed caches).
+__device__ __forceinline__ void lds_dma16_nt(const uint16_t* g, const uint16_t* lds_run) {
+  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_run);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(base) : "memory");
+}
 
 // The same with the run starting at LDS byte address m0 (uniform).
 __device__ __forceinline__ void lds_dma16s(const uint16_t* g, unsigned m0) {
