@@ -378,7 +378,9 @@ def secondary(bda, synth, torch, dev, args):
 
     # ---- row statistics (confidence, argmax, entropy) on the same logits
     sws = torch.empty(bda.lib.bda_row_stats_workspace_bytes(G, R, V), dtype=torch.uint8, device=dev)
-    mean, med = time_launches(lambda i: bda.row_stats(sets[i % 3], workspace=sws), iters, 5)
+    souts = (torch.empty(G, R, device=dev), torch.empty(G, R, dtype=torch.int64, device=dev),
+             torch.empty(G, R, device=dev), torch.empty(G, device=dev))
+    mean, med = time_launches(lambda i: bda.row_stats(sets[i % 3], workspace=sws, out=souts), iters, 5)
     res["row_stats"] = {"G": G, "R": R, "V": V, "us_per_call": round(mean * 1e3, 2),
                         "GB/s": round(byts / (mean * 1e-3) / 1e9, 1),
                         "hbm_frac": round(byts / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

@@ -373,12 +373,13 @@ def verify(logits, drafts, workspace=None):
     return am, acc
 
 
-def row_stats(logits, masked=None, workspace=None):
+def row_stats(logits, masked=None, workspace=None, out=None):
     """Per-row softmax statistics of logits [G,R,V] (bf16 or fp32): returns
     (conf [G,R] float32, argmax [G,R] int64, entropy [G,R] float32 in nats,
     mean_entropy [G] float32).  With ``masked`` (uint8 [G,R]) only rows with
     masked != 0 are computed; the other rows' outputs are NaN / -1 and the
-    group means cover the computed rows only."""
+    group means cover the computed rows only.  ``out`` = the four output
+    tensors, written in place (rows not computed keep their contents)."""
     if logits.dim() != 3:
         raise ValueError("logits must be [G, R, V]")
     G, R, V = logits.shape
@@ -388,10 +389,18 @@ def row_stats(logits, masked=None, workspace=None):
     if masked is not None and (masked.dtype != torch.uint8 or tuple(masked.shape) != (G, R)):
         raise ValueError("masked must be uint8 [G, R]")
     dev = _check_dev(logits, masked)
-    conf = torch.full((G, R), float("nan"), dtype=torch.float32, device=dev)
-    am = torch.full((G, R), -1, dtype=torch.int64, device=dev)
-    ent = torch.full((G, R), float("nan"), dtype=torch.float32, device=dev)
-    mean = torch.empty(G, dtype=torch.float32, device=dev)
+    if out is not None:
+        conf, am, ent, mean = out
+        for t, dt_, shp in ((conf, torch.float32, (G, R)), (am, torch.int64, (G, R)), (ent, torch.float32, (G, R)),
+                            (mean, torch.float32, (G,))):
+            if t.dtype != dt_ or tuple(t.shape) != shp or not t.is_contiguous() or t.device != dev:
+                raise ValueError("out tensors must be contiguous conf/entropy float32 [G,R], argmax int64 [G,R], "
+                                 "mean float32 [G] on the logits' device")
+    else:
+        conf = torch.full((G, R), float("nan"), dtype=torch.float32, device=dev)
+        am = torch.full((G, R), -1, dtype=torch.int64, device=dev)
+        ent = torch.full((G, R), float("nan"), dtype=torch.float32, device=dev)
+        mean = torch.empty(G, dtype=torch.float32, device=dev)
     need = int(lib.bda_row_stats_workspace_bytes(G, R, V))
     ws = _workspace(need, dev, workspace)
     rc = lib.bda_row_stats(_ptr(logits), dt, _ptr(masked), _ptr(conf), _ptr(am), _ptr(ent), _ptr(mean),
