@@ -12,11 +12,12 @@
 //   dq     query-stationary, like the forward: per key tile S^T = K Q^T,
 //          dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T (K^T by the LDS
 //          transpose read, dS^T straight from the accumulator registers).
-//   dkdv   key-stationary: a workgroup keeps 128 keys (32 per wavefront) of
-//          one (batch, kv head) in LDS and streams the blocks of 32 query
-//          slots (rows x heads of the group) that see them:
-//          S = Q K^T, dP = dO V^T (lane = key), dV += P^T dO and
-//          dK += dS^T Q (dO and Q by the LDS transpose read).
+//   dkdv   key-stationary: a workgroup keeps 128 keys of one (batch, kv
+//          head) in LDS and streams the blocks of 32 query slots (rows x
+//          heads of the group) that see them; two groups of 4 wavefronts (32
+//          keys each) take alternate blocks: S = Q K^T, dP = dO V^T
+//          (lane = key), dV += P^T dO and dK += dS^T Q (dO and Q by the LDS
+//          transpose read); the groups' partial dK, dV add at the end.
 // P is rebuilt exactly from the log-sum-exp (no running max); masked pairs
 // get P = 0.  fp32 accumulation, bf16 MFMA operands, bf16 gradients.
 #include <limits.h>
@@ -279,29 +280,37 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV.  One workgroup of 4 wavefronts per (batch, kv head, 128-key tile of
-// one half); wavefront w owns keys 32w .. 32w+31 of the tile.  The query
-// slots that see the tile are streamed in blocks of 32 (rows x the G heads
-// of the kv head), staged in LDS through registers, double-buffered.
+// dK, dV with two wavefronts per SIMD.  One workgroup of 8 wavefronts per
+// (batch, kv head, 128-key tile of one half); wavefronts w and w + 4 own keys
+// 32(w%4) .. 32(w%4)+31 of the tile and form two groups: at step s group g
+// computes query block 2s + g.  K and V stay in LDS and are read per block
+// (a wavefront keeps only its dK, dV accumulators), four single-block stages
+// hold the two blocks being computed and the two loading for the next step.
+// At the end group 1 adds its dK, dV partials into group 0's through LDS.
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
   constexpr int KSTEPS = D / 16, DT = D / 32, CPR = D / 8;
-  constexpr int TK = 128, NT = 256;
+  constexpr int TK = 128, NT = 512;
   constexpr int KE = TK * D;                   // elements of the K (or V) tile
   constexpr int QE = 32 * D;                   // elements of a Q (or dO) block
   constexpr int QCH = 32 * CPR;                // chunks of a Q block
-  __shared__ __attribute__((aligned(16))) uint16_t kv[2 * KE];
-  constexpr int NS = 4;                        // query-block stages, filled three blocks ahead
-  __shared__ __attribute__((aligned(16))) uint16_t qd[NS][2 * QE];
+  constexpr int NS = 4;                        // single-block stages
+  // [K tile | V tile | NS x (Q block | dO block)]; reused for the merge and
+  // the transposed write of dK, dV at the end
+  constexpr int LDS_ELEMS = 2 * KE + NS * 2 * QE;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
+  uint16_t* const kv = lds;
+  uint16_t* const qd = lds + 2 * KE;
   __shared__ __attribute__((aligned(16))) float sl[NS][2][32];  // lse (natural log), delta per slot
   // Per slot, the mask as one integer t: clean-key tiles let a slot see key
   // block kb iff kb <= t (t = the row's block for an x_0 row, one less for
   // an x_t row); noisy-key tiles iff kb == t (t = the row's block for an
   // x_t row).  t = -1: no such row, or a row that sees nothing of the tile.
   __shared__ __attribute__((aligned(16))) int sthr[NS][32];
+  static_assert(4 * 2 * DT * 16 * 64 * 4 <= LDS_ELEMS * 2, "merge buffer exceeds LDS");
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, ql = lane & 31, hb = lane >> 5;
-  const int nk = 2 * a.nkh;
+  const int kg = w >> 2, wk = w & 3;           // query-block group, key group
   int pair, j;
   {
     const int bid = blockIdx.x;
@@ -315,13 +324,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
       j = bid / P;
     }
   }
-  (void)nk;
-  // heaviest first: clean (x_0) tiles from the start of the sequence, then
-  // the noisy (x_t) tiles, which only their own blocks' rows see
   const bool clean = j < a.nkh;
-  const int kp0 = (clean ? j : j - a.nkh) * TK;          // first key position of the tile
+  const int kp0 = (clean ? j : j - a.nkh) * TK;
   const int kp1 = imin(a.L, kp0 + TK);
-  const int kbase_row = (clean ? a.L : 0) + kp0;        // key-tensor row of the tile's first key
+  const int kbase_row = (clean ? a.L : 0) + kp0;
   const int b = pair / a.Hkv, g = pair - b * a.Hkv;
   const size_t kvoff = (size_t)pair * a.S * D;
 
@@ -336,36 +342,31 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     *(u32x4*)(kv + KE + lo) = *(const u32x4*)(a.v + off);
   }
 
-  // query rows that see the tile: up to two position ranges
+  // query rows that see the tile: up to two position ranges, [ra0, ra1) of
+  // half ha and [rb0, rb1) of x_t; heaviest tiles first (clean tiles from
+  // the start of the sequence, then the noisy tiles, which only their own
+  // blocks' rows see)
   const int jb = kp0 / a.blk;
-  int ra0, ra1, rb0, rb1;                       // positions [ra0, ra1) of half ha, [rb0, rb1) of x_t
-  int ha;
+  int ra0, ra1, rb0, rb1, ha;
   if (clean) {
-    ha = 1;                                     // x_0 rows of blocks >= jb
+    ha = 1;
     ra0 = jb * a.blk;
     ra1 = a.L;
-    rb0 = imin(a.L, (jb + 1) * a.blk);          // x_t rows of blocks > jb
+    rb0 = imin(a.L, (jb + 1) * a.blk);
     rb1 = a.L;
   } else {
-    ha = 0;                                     // x_t rows of the tile's own blocks
+    ha = 0;
     ra0 = jb * a.blk;
     ra1 = imin(a.L, ((kp1 - 1) / a.blk + 1) * a.blk);
     rb0 = rb1 = 0;
   }
-  const int rpb = 32 / a.G;                     // rows per block of 32 slots
+  const int rpb = 32 / a.G;
   const int na = ra1 > ra0 ? (ra1 - ra0 + rpb - 1) / rpb : 0;
   const int nb = rb1 > rb0 ? (rb1 - rb0 + rpb - 1) / rpb : 0;
   const int nblk = na + nb;
 
-  // Block t of query slots straight from global memory into LDS stage st:
-  // Q and dO rows (each lane loads the 16-byte chunk the permuted layout puts
-  // at its lane slot), then the slots' lse and delta (one dword per lane of
-  // lanes 0..15 of every wavefront: dwords 16w .. 16w+15 of lse[32] ++
-  // delta[32]).  Slots without a row load row 0 of the block (finite data
-  // the thresholds never let through).  Every wavefront issues the same
-  // number of loads, so one vmcnt bound serves all.
   constexpr int QRUNS = QCH / 64;                         // 64-chunk runs of a Q block
-  constexpr int QJ = (QRUNS + 3) / 4;                     // runs per wavefront per matrix
+  constexpr int QJ = (QRUNS + 3) / 4;                     // runs per wavefront of a group per matrix
   auto block_row0 = [&](int t, int& half, int& r0, int& r1) {
     if (t < na) {
       half = ha;
@@ -377,15 +378,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
       r1 = rb1;
     }
   };
-  const unsigned lds_qd = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)&qd[0][0]);
+  const unsigned lds_qd = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)qd);
   const unsigned lds_sl = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)&sl[0][0][0]);
+  // Block t of query slots straight from global memory into LDS stage st,
+  // issued by the 4 wavefronts of one group: Q and dO rows (each lane loads
+  // the 16-byte chunk the permuted layout puts at its lane slot), then the
+  // slots' lse and delta (one dword per lane of lanes 0..15 of every
+  // wavefront of the group: dwords 16wk .. 16wk+15 of lse[32] ++ delta[32]),
+  // then the slots' thresholds.  Slots without a row load row 0 of the block
+  // (finite data the thresholds never let through).
   auto issue = [&](int t, int st) {
-    t = imin(t, nblk - 1);                      // past the end: repeat the last block (never computed)
     int half, r0, r1;
     block_row0(t, half, r0, r1);
 #pragma unroll
     for (int q = 0; q < QJ; ++q) {
-      const int run = imin(w + 4 * q, QRUNS - 1);   // spare wavefronts repeat the last run
+      const int run = imin(wk + 4 * q, QRUNS - 1);
       const int pos = run * 64 + lane;
       const int sl_ = pos / CPR, c = (pos % CPR) ^ (swz<D>(sl_) & (CPR - 1));
       const int rl = sl_ / a.G;
@@ -397,32 +404,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
       lds_dma16s(a.dout + off, dst + QE * 2);
     }
     {
-      const int x = 16 * w + (lane & 15);       // dword of lse[32] ++ delta[32]
+      const int x = 16 * wk + (lane & 15);
       const int slot = x & 31;
       const int rl = slot / a.G;
       const bool ok = rl < rpb && r0 + rl < r1;
       const int head = g * a.G + (ok ? slot - rl * a.G : 0);
       const size_t ri = (size_t)(b * a.Hq + head) * a.S + half * a.L + (ok ? r0 + rl : r0);
       const float* src = (x < 32 ? a.lse : a.delta) + ri;
-      if (lane < 16) lds_dma4s(src, lds_sl + (unsigned)(st * 64 + 16 * w) * 4);
+      if (lane < 16) lds_dma4s(src, lds_sl + (unsigned)(st * 64 + 16 * wk) * 4);
     }
-    if (tid < 32) {                             // the slots' mask thresholds
-      const int rl = tid / a.G, pos = r0 + rl;
+    if ((tid & 255) < 32) {
+      const int s_ = tid & 255, rl = s_ / a.G, pos = r0 + rl;
       int t_ = -1;
       if (rl < rpb && pos < r1) {
         const int rb = pos / a.blk;
         t_ = clean ? (half == 1 ? rb : rb - 1) : (half == 0 ? rb : -1);
       }
-      sthr[st][tid] = t_;
+      sthr[st][s_] = t_;
     }
   };
-  auto settle = [&]() {
-    constexpr int N = 2 * QJ + 1;               // this block's loads stay in flight
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  };
+  // every load of this wavefront (DMA included) and every LDS access done,
+  // then the workgroup barrier
   auto drain = [&]() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0);
@@ -430,15 +432,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     asm volatile("" ::: "memory");
   };
 
-  // lane constants: my key, and the transpose-read offsets
-  const int key = kp0 + 32 * w + ql;            // position of my key in its half
+  const int key = kp0 + 32 * wk + ql;
   const bool key_ok = key < kp1;
-  const int kblk = key_ok ? key / a.blk : INT_MAX / 2;   // my key's block (past the end: never seen)
-  // the wavefront's key blocks, for whole-block decisions
-  const int wk0 = kp0 + 32 * w, wk1 = imin(kp1, wk0 + 32);
+  const int kblk = key_ok ? key / a.blk : INT_MAX / 2;
+  const int wk0 = kp0 + 32 * wk, wk1 = imin(kp1, wk0 + 32);
   const int wb0 = wk0 / a.blk, wb1 = wk1 > wk0 ? (wk1 - 1) / a.blk : -1;
-  const int kr_off = (32 * w + ql) * D;          // my key's row in the K / V tile
-  const int k_swz = swz<D>(32 * w + ql) & (CPR - 1);
+  const int kr_off = (32 * wk + ql) * D;
+  const int k_swz = swz<D>(32 * wk + ql) & (CPR - 1);
   const int q_swz = swz<D>(ql) & (CPR - 1);
   int t_lo[DT], t_hi[DT];
   {
@@ -452,46 +452,31 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     }
   }
 
-  bf16x8 kop[KSTEPS], vop[KSTEPS];              // my key's K and V operands (read once from LDS)
   f32x16 dka[DT], dva[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dka[dt] = dva[dt] = f32x16{};
 
-  // Whether every slot of stage st sees every key of the wavefront (then no
-  // per-element mask is needed).  A block the wavefront cannot see at all
-  // gets P = dS = 0 from the per-slot thresholds.
   const bool full_wave = wk1 - wk0 == 32;
   auto seen_all = [&](int st) -> bool {
     const int my_t = sthr[st][ql];
     const bool lane_ok = clean ? my_t >= wb1 : (wb0 == wb1 && my_t == wb0);
     return full_wave && __all(lane_ok);
   };
-  // S^T-shaped scores and dP of the query block in stage st
-  auto sdp = [&](int st, f32x16& sv, f32x16& dp) {
-    const uint16_t* qb = &qd[st][0];
-    const uint16_t* db = &qd[st][QE];
-    sv = f32x16{};
-    dp = f32x16{};
+  // the query block in stage st: S, dP (K and V operands from LDS), then P,
+  // dS and the dV, dK updates
+  auto block = [&](int st) {
+    const uint16_t* qb = qd + st * 2 * QE;
+    const uint16_t* db = qb + QE;
+    const bool all_seen = seen_all(st);
+    f32x16 sv{}, dp{};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      const bf16x8 qa = *(const bf16x8*)(qb + ql * D + 8 * ((2 * ks + hb) ^ q_swz));
-      const bf16x8 da = *(const bf16x8*)(db + ql * D + 8 * ((2 * ks + hb) ^ q_swz));
-      sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kop[ks], sv, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vop[ks], dp, 0, 0, 0);
-    }
-  };
-  // P, dS and the dV, dK updates of the query block in stage st
-  auto grads = [&](int st, const f32x16& sv, const f32x16& dp, bool all_seen) {
-    const uint16_t* qb = &qd[st][0];
-    const uint16_t* db = &qd[st][QE];
-    // lane = key (column), value i = slot 8*(i/4) + 4*hb + (i%4)
-    f32x4 l4[4], d4[4];
-    i32x4 t4[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      l4[u] = *(const f32x4*)(&sl[st][0][8 * u + 4 * hb]) * kLn2Inv;
-      d4[u] = *(const f32x4*)(&sl[st][1][8 * u + 4 * hb]);
-      t4[u] = *(const i32x4*)(&sthr[st][8 * u + 4 * hb]);
+      const int ko = kr_off + 8 * ((2 * ks + hb) ^ k_swz);
+      const int qo = ql * D + 8 * ((2 * ks + hb) ^ q_swz);
+      sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qb + qo), *(const bf16x8*)(kv + ko), sv, 0, 0,
+                                                  0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(db + qo), *(const bf16x8*)(kv + KE + ko), dp, 0,
+                                                  0, 0);
     }
     bf16x8 pb[2], sb[2];
 #pragma unroll
@@ -503,11 +488,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int i = 8 * kk + 2 * e2 + h;
-          const int t = t4[i >> 2][i & 3];
+          const int slot = 8 * (i >> 2) + 4 * hb + (i & 3);
+          const int t = sthr[st][slot];
           const bool ok = all_seen || (clean ? kblk <= t : kblk == t);
-          const float p = ok ? exp2_fast(fmaf(sv[i], a.sl2, -l4[i >> 2][i & 3])) : 0.f;
+          const float p = ok ? exp2_fast(fmaf(sv[i], a.sl2, -sl[st][0][slot] * kLn2Inv)) : 0.f;
           pv[h] = p;
-          dv2[h] = p * (dp[i] - d4[i >> 2][i & 3]);
+          dv2[h] = p * (dp[i] - sl[st][1][slot]);
         }
         pk[e2] = pack_bf16x2(pv[0], pv[1]);
         dk4[e2] = pack_bf16x2(dv2[0], dv2[1]);
@@ -515,7 +501,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
       pb[kk] = __builtin_bit_cast(bf16x8, pk);
       sb[kk] = __builtin_bit_cast(bf16x8, dk4);
     }
-    // dV += P^T dO, dK += dS^T Q (slots {16kk + 4hb + 0..3, +8} by transpose reads)
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
@@ -532,59 +517,66 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     }
   };
 
-  if (nblk > 0) {
-    issue(0, 0);
-    issue(1, 1);
-    issue(2, 2);
-    drain();
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      kop[ks] = *(const bf16x8*)(kv + kr_off + 8 * ((2 * ks + hb) ^ k_swz));
-      vop[ks] = *(const bf16x8*)(kv + KE + kr_off + 8 * ((2 * ks + hb) ^ k_swz));
-    }
-    // Software-pipelined over query blocks: the S and dP MFMAs of block t + 1
-    // are issued with the P / dS arithmetic and the dV / dK MFMAs of block t
-    // (one wavefront per SIMD, so the overlap has to come from within it).
-    // Block t + 1 is visible here: the settle of the previous step left only
-    // the newest block (t + 2) in flight.
-    f32x16 sv0, dp0, sv1, dp1;
-    sdp(0, sv0, dp0);
-    bool all0 = seen_all(0);
+  // Block t lives in stage t % NS.  Step s: group g issues block 2s + 2 + g
+  // into the stage of block 2s - 2 + g (finished before the last barrier),
+  // computes block 2s + g, then every load lands before the barrier.
+  if (kg < nblk) issue(kg, kg);
+  drain();   // also publishes the K, V tile
+  const int nsteps = (nblk + 1) / 2;
 #pragma unroll 1
-    for (int t = 0; t < nblk; ++t) {
-      sdp((t + 1) % NS, sv1, dp1);             // past the last block: stale data, never used
-      grads(t % NS, sv0, dp0, all0);
-      const bool all1 = seen_all((t + 1) % NS);
-      issue(t + 3, (t + 3) % NS);              // into the stage of block t - 1, free since the last barrier
-      settle();
-      sv0 = sv1;
-      dp0 = dp1;
-      all0 = all1;
-    }
+  for (int s = 0; s < nsteps; ++s) {
+    const int tn = 2 * s + 2 + kg, tc = 2 * s + kg;
+    if (tn < nblk) issue(tn, tn % NS);
+    if (tc < nblk) block(tc % NS);
+    drain();
   }
-  drain();
 
-  // write dK (scaled) and dV: accumulator lane (ql, hb) holds column
-  // d = 32*dt + ql and keys 8*(i/4) + 4*hb + (i%4) of the wavefront's 32;
-  // transposed through LDS into 16-byte rows
-  uint16_t* tk = kv + w * 2 * 32 * D;           // this wavefront's 2 x [32 keys][D]
-  uint16_t* tv = tk + 32 * D;
+  // group 1 adds its partials into group 0's through LDS
+  float* xf = reinterpret_cast<float*>(lds);
+  auto xi = [&](int which, int dt, int i) { return (((wk * 2 + which) * DT + dt) * 16 + i) * 64 + lane; };
+  if (kg == 1) {
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kr = 8 * (i >> 2) + 4 * hb + (i & 3);
-      tk[kr * D + 32 * dt + ql] = __builtin_bit_cast(uint16_t, (__bf16)(dka[dt][i] * a.scale));
-      tv[kr * D + 32 * dt + ql] = __builtin_bit_cast(uint16_t, (__bf16)dva[dt][i]);
-    }
+      for (int i = 0; i < 16; ++i) {
+        xf[xi(0, dt, i)] = dka[dt][i];
+        xf[xi(1, dt, i)] = dva[dt][i];
+      }
+  }
   __syncthreads();
-  for (int ch = lane; ch < 32 * CPR; ch += 64) {
-    const int kr = ch / CPR, c = ch % CPR;
-    const int kpos = kp0 + 32 * w + kr;
-    if (kpos < kp1) {
-      const size_t off = kvoff + (size_t)((clean ? a.L : 0) + kpos) * D + 8 * c;
-      *(u32x4*)(a.dk + off) = *(const u32x4*)(tk + kr * D + 8 * c);
-      *(u32x4*)(a.dv + off) = *(const u32x4*)(tv + kr * D + 8 * c);
+  if (kg == 0) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        dka[dt][i] += xf[xi(0, dt, i)];
+        dva[dt][i] += xf[xi(1, dt, i)];
+      }
+  }
+  __syncthreads();
+  // write dK (scaled) and dV through LDS into 16-byte rows (group 0)
+  uint16_t* tk = lds + wk * 2 * 32 * D;
+  uint16_t* tv = tk + 32 * D;
+  if (kg == 0) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kr = 8 * (i >> 2) + 4 * hb + (i & 3);
+        tk[kr * D + 32 * dt + ql] = __builtin_bit_cast(uint16_t, (__bf16)(dka[dt][i] * a.scale));
+        tv[kr * D + 32 * dt + ql] = __builtin_bit_cast(uint16_t, (__bf16)dva[dt][i]);
+      }
+  }
+  __syncthreads();
+  if (kg == 0) {
+    for (int ch = lane; ch < 32 * CPR; ch += 64) {
+      const int kr = ch / CPR, c = ch % CPR;
+      const int kpos = kp0 + 32 * wk + kr;
+      if (kpos < kp1) {
+        const size_t off = kvoff + (size_t)((clean ? a.L : 0) + kpos) * D + 8 * c;
+        *(u32x4*)(a.dk + off) = *(const u32x4*)(tk + kr * D + 8 * c);
+        *(u32x4*)(a.dv + off) = *(const u32x4*)(tv + kr * D + 8 * c);
+      }
     }
   }
 }
@@ -636,7 +628,7 @@ static hipError_t bwd_launch_d(const BwdPlan& p, const BwdArgs& a, hipStream_t s
     hipLaunchKernelGGL((bwd_dq_kernel<D, 4>), dim3((unsigned)p.grid_dq), dim3(256), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)p.grid_kv), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)p.grid_kv), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 
