@@ -54,31 +54,41 @@ def causal_pairs(L, n):
     return n * (L - n) + n * (n + 1) // 2
 
 
-_SLEEP_CYCLES_PER_MS = None
+_FILL = None   # (source, destination, ms per copy) of the queue filler
 
 
-def _sleep_cycles_per_ms():
-    """GPU spin cycles per millisecond of torch.cuda._sleep, measured once."""
-    global _SLEEP_CYCLES_PER_MS
-    if _SLEEP_CYCLES_PER_MS is None:
-        import torch
+def _queue_fill(ms):
+    """Keep the GPU streaming memory for about ms milliseconds: device copies
+    between two 512 MB buffers, enqueued in well under a millisecond.  A GPU
+    left nearly idle instead (a one-workgroup spin) lets the memory-side
+    clocks drop, and HBM-bound calls queued behind it then ran ~15% slower
+    than in steady state (decode attention 127 against 110 us)."""
+    global _FILL
+    import torch
+    if _FILL is None:
+        src = torch.zeros(1 << 28, dtype=torch.float16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(1000)
         a.record()
-        torch.cuda._sleep(1_000_000)
+        for _ in range(5):
+            dst.copy_(src)
         b.record()
         torch.cuda.synchronize()
-        _SLEEP_CYCLES_PER_MS = 1_000_000 / max(a.elapsed_time(b), 1e-3)
-    return _SLEEP_CYCLES_PER_MS
+        _FILL = (src, dst, max(a.elapsed_time(b) / 5, 1e-3))
+    src, dst, per = _FILL
+    for _ in range(int(ms / per) + 1):
+        dst.copy_(src)
 
 
 def time_launches(fn, iters, warmup, pre=None, queue=True):
     """Mean and median per-launch ms of fn(i) with HIP events on the current
-    stream.  The timed launches are queued behind a GPU sleep long enough for
-    the host to enqueue all of them, so each event pair measures the GPU's
-    back-to-back time for the call and not the host's launch overhead (the
-    ctypes call and argument checks take tens of microseconds, as long as a
-    small kernel).  queue=False times each call as the host issues it."""
+    stream.  The timed launches are queued behind enough memory-streaming
+    work for the host to enqueue all of them, so each event pair measures the
+    GPU's back-to-back time for the call and not the host's launch overhead
+    (the ctypes call and argument checks take tens of microseconds, as long
+    as a small kernel).  queue=False times each call as the host issues it."""
     import time
     import torch
     t0 = time.perf_counter()
@@ -91,7 +101,7 @@ def time_launches(fn, iters, warmup, pre=None, queue=True):
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
     if queue:
-        torch.cuda._sleep(int(_sleep_cycles_per_ms() * min(2.0 * host_ms * iters + 1.0, 200.0)))
+        _queue_fill(min(2.0 * host_ms * iters + 1.0, 200.0))
     for i in range(iters):
         if pre:
             pre(i)
