@@ -58,11 +58,13 @@ struct Geom {
 // One workgroup = NW wavefronts; a wavefront owns QPW query slots, handled as
 // QPW/32 MFMA column blocks that share every K and V operand read from LDS
 // (64 slots per wavefront halve the LDS traffic per FLOP of 32).
-// STAGES = 4: the DMA-fed pipelined walk (one 8-wave workgroup per CU at
-// d = 128) for long query ranges (training form, prefill).
-// STAGES = 2: a register-staged double-buffered walk whose smaller LDS
-// footprint lets two 4-wave workgroups share a CU, for short query blocks
-// over long caches (decode, verify).
+// STAGES = 4: the persistent DMA-fed pipelined walk (one 8-wave workgroup
+// per CU at d = 128) for long query ranges (training form, prefill).
+// STAGES = 5: the split-key DMA ring for short query blocks over long caches
+// (decode, verify): one 8-wave workgroup per item, two groups of 4 over the
+// same query slots, each computing one 32-key half of every tile.
+// STAGES = 2: a register-staged double-buffered walk with 4-wave workgroups
+// for short training-form sequences (L < 256).
 template <int D, int NW, int QPW, int STAGES, bool VARLEN, bool LSE>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) {
   constexpr int NQB = QPW / 32;               // 32-query column blocks per wavefront
