@@ -546,6 +546,42 @@ __global__ __launch_bounds__(kCommitThreads) void commit_entropy_finalize_kernel
     sh[r] = h;
     sa[r] = a;
   }
+  if (R <= 64) {
+    // One wavefront ranks the group in registers: lane r holds row r; ranks
+    // by (H, row) from lane reads, then the rows in rank order and their
+    // entropies summed in that order, as below.
+    __syncthreads();                             // publishes sh, sa
+    if (tid >= 64) return;
+    const bool in = tid < R;
+    const float h = in ? sh[tid] : INFINITY;
+    const int av = in ? sa[tid] : -1;
+    const bool live = av >= 0;
+    int rank = 0;
+    for (int o = 0; o < R; ++o) {
+      const float ho = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h), o));
+      rank += (ho < h) || (ho == h && o < tid);
+    }
+    int inv = 0;                                 // lane k: the row of rank k
+    for (int o = 0; o < R; ++o) {
+      const int ro = __builtin_amdgcn_readlane(rank, o);
+      const int lo = __builtin_amdgcn_readlane(live ? 1 : 0, o);
+      if (lo && ro == tid) inv = o;
+    }
+    const int nmask = __popcll(__ballot(live));
+    float acc = 0.f;
+    int n = 0;
+    for (int k = 0; k < nmask; ++k) {
+      const int src = __builtin_amdgcn_readlane(inv, k);
+      acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h), src));
+      if (acc <= bound) n = k + 1;
+      else break;
+    }
+    if (live && rank < max(n, min(k_min, nmask))) {
+      tokens[base + tid] = av;
+      masked[base + tid] = 0;
+    }
+    return;
+  }
   const int nmask = block_sum(nm, red);          // (its barriers also publish sh, sa)
   for (int r = tid; r < R; r += kCommitThreads) {
     if (sa[r] < 0) continue;

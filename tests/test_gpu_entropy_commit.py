@@ -81,6 +81,8 @@ def _run(logits, masked, bound, temperature, k_min, what):
     (3, 4, 37, 1000, 0.4, 2, torch.float32),      # ragged rows and vocabulary, fp32 logits
     (4, 3, 256, 4096, 2.0, 0, torch.bfloat16),
     (5, 2, 1, 50000, 1.0, 1, torch.bfloat16),     # one row per group
+    (8, 3, 64, 2048, 1.0, 3, torch.bfloat16),     # largest group ranked by one wavefront
+    (9, 2, 65, 2048, 0.7, 1, torch.bfloat16),     # smallest group ranked by the whole workgroup
 ])
 def test_entropy_commit(case):
     seed, G, R, V, T, k_min, dt = case
