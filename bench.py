@@ -126,6 +126,17 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_each_way": n, "launches": 5}))
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline_attention(case, budget_s=20.0):
     """The oracle, untuned, on a bounded sample of the same workload: every
     row of the query heads of the first kv head(s) of batch 0, the number of
@@ -151,7 +162,7 @@ def cpu_baseline_attention(case, budget_s=20.0):
         else:
             nb = min(B, nb * 2)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": f"all {rows} rows of {heads} query heads ({kvh} kv heads) of {nb} batch(es) "
+            "cpu": _cpu_model(), "sample": f"all {rows} rows of {heads} query heads ({kvh} kv heads) of {nb} batch(es) "
                       f"({flops / 1e9:.1f} GFLOP, {dt:.1f} s)"}
 
 
@@ -166,7 +177,7 @@ def cpu_baseline_commit(logits, masked, tau, k_min):
     dt = time.perf_counter() - t0
     committed = int(masked[:g].numpy().sum() - m.sum())
     return {"value": committed / dt, "unit": "committed tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": f"{g} of {G} groups ({committed} tokens, {dt:.2f} s)"}
+            "cpu": _cpu_model(), "sample": f"{g} of {G} groups ({committed} tokens, {dt:.2f} s)"}
 
 
 def main():
