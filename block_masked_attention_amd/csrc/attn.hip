@@ -488,7 +488,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int jj = e0 + 8 * (i >> 2) + 4 * hb + (i & 3);
-            const bool ok = jj < e1 && (in_span(A[qb], jj) || in_span(C[qb], jj));
+            const bool ok = (jj < e1) & (in_span(A[qb], jj) | in_span(C[qb], jj));   // a select, no branches
             s[qb][i] = ok ? s[qb][i] : -INFINITY;
           }
         }

@@ -225,8 +225,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdArgs a) {
         for (int h = 0; h < 2; ++h) {
           const int i = 8 * kk + 2 * e2 + h;
           const int jj = e0 + 8 * (i >> 2) + 4 * hb + (i & 3);
-          const bool ok = full || (jj < e1 && (in_span(A, jj) || in_span(C, jj)));
-          const float p = ok ? exp2_fast(fmaf(sv[i], a.sl2, -lse2)) : 0.f;
+          // bitwise, not short-circuit: a select per element, no branches
+          const bool ok = full | ((jj < e1) & (in_span(A, jj) | in_span(C, jj)));
+          const float p = exp2_fast(ok ? fmaf(sv[i], a.sl2, -lse2) : -INFINITY);   // masked: exp2(-inf) = 0
           d2[h] = p * (dp[i] - dl);
         }
         pk[e2] = pack_bf16x2(d2[0], d2[1]);
@@ -478,9 +479,23 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(db + qo), *(const bf16x8*)(kv + KE + ko), dp, 0,
                                                   0, 0);
     }
+    // lane = key (column), value i = slot 8*(i/4) + 4*hb + (i%4).  The
+    // slots' lse, delta and threshold are read as 4-vectors, half a block at
+    // a time, so the reads are unconditional and masked pairs take
+    // exp2(-inf) = 0 by a select (per-element reads were sunk into a branch
+    // and a full LDS wait per element).
     bf16x8 pb[2], sb[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
+      f32x4 lv[2], dvv[2];
+      i32x4 tv[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int o = 8 * (2 * kk + u) + 4 * hb;
+        lv[u] = *(const f32x4*)(&sl[st][0][o]) * kLn2Inv;
+        dvv[u] = *(const f32x4*)(&sl[st][1][o]);
+        tv[u] = *(const i32x4*)(&sthr[st][o]);
+      }
       u32x4 pk, dk4;
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
@@ -488,12 +503,12 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int i = 8 * kk + 2 * e2 + h;
-          const int slot = 8 * (i >> 2) + 4 * hb + (i & 3);
-          const int t = sthr[st][slot];
-          const bool ok = all_seen || (clean ? kblk <= t : kblk == t);
-          const float p = ok ? exp2_fast(fmaf(sv[i], a.sl2, -sl[st][0][slot] * kLn2Inv)) : 0.f;
+          const int u = (2 * e2 + h) >> 2, x = i & 3;
+          const int t = tv[u][x];
+          const bool ok = all_seen | (clean & (kblk <= t)) | (!clean & (kblk == t));
+          const float p = exp2_fast(ok ? fmaf(sv[i], a.sl2, -lv[u][x]) : -INFINITY);
           pv[h] = p;
-          dv2[h] = p * (dp[i] - sl[st][1][slot]);
+          dv2[h] = p * (dp[i] - dvv[u][x]);
         }
         pk[e2] = pack_bf16x2(pv[0], pv[1]);
         dk4[e2] = pack_bf16x2(dv2[0], dv2[1]);
