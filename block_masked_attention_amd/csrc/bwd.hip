@@ -78,8 +78,9 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdArgs a) {
   constexpr int KSTEPS = D / 16, DT = D / 32, CPR = D / 8;
-  constexpr int BN = 64, TCH = BN * CPR, NT = NW * 64, CU = (TCH + NT - 1) / NT, TE = BN * D;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TE];
+  constexpr int BN = 64, TCH = BN * CPR, NT = NW * 64, TE = BN * D;
+  constexpr int NSQ = 4;                       // K/V tile stages, filled three tiles ahead
+  __shared__ __attribute__((aligned(16))) uint16_t smem[NSQ * 2 * TE];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, ql = lane & 31, hb = lane >> 5;
   const int P = a.B * a.Hkv;
@@ -166,54 +167,63 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdArgs a) {
     }
   }
 
-  u32x4 kreg[CU], vreg[CU];
-  auto fetch = [&](int j) {
+  // Tile j straight from global memory into stage st (no registers): lane i
+  // of a wavefront's load lands 16 bytes at its slot of a contiguous 1 KB
+  // run, so it loads the chunk the permuted layout puts there.
+  constexpr int DJ = TCH >= NT ? TCH / NT : 1;   // loads per wavefront per matrix
+  auto issue = [&](int j, uint16_t* st) {
     int t0, t1;
     tile(j, t0, t1);
 #pragma unroll
-    for (int u = 0; u < CU; ++u) {
-      const int ch = tid + u * NT;
-      if (TCH % NT == 0 || ch < TCH) {
-        const int r = ch / CPR, c = ch % CPR;
+    for (int q = 0; q < DJ; ++q) {
+      const int run = w * DJ + q;
+      if (run * 64 < TCH) {
+        const int pos = run * 64 + lane;
+        const int r = pos / CPR, c = (pos % CPR) ^ (swz<D>(pos / CPR) & (CPR - 1));
         const size_t off = (size_t)imin(t0 + r, t1 - 1) * D + 8 * c;
-        kreg[u] = *(const u32x4*)(kbase + off);
-        vreg[u] = *(const u32x4*)(vbase + off);
+        uint16_t* dst = st + run * 64 * 8;
+        lds_dma16(kbase + off, dst);
+        lds_dma16(vbase + off, dst + TE);
       }
     }
   };
-  auto lstore = [&](uint16_t* st) {
-#pragma unroll
-    for (int u = 0; u < CU; ++u) {
-      const int ch = tid + u * NT;
-      if (TCH % NT == 0 || ch < TCH) {
-        const int off = chunk_off<D>(ch / CPR, ch % CPR);
-        *(u32x4*)(st + off) = kreg[u];
-        *(u32x4*)(st + TE + off) = vreg[u];
-      }
-    }
+  // Tile j visible to every wavefront, given that tiles 0 .. issued-1 have
+  // been issued: the (up to two) tiles issued after j stay in flight.
+  auto settle_for = [&](int j, int issued) {
+    const int newer = imin(NSQ - 2, imax(0, issued - 1 - j));
+    constexpr int T = 2 * DJ;
+    asm volatile("" ::: "memory");
+    if (newer >= 2)
+      __builtin_amdgcn_s_waitcnt(((2 * T) & 15) | (7 << 4) | (((2 * T) >> 4) << 14));
+    else if (newer == 1)
+      __builtin_amdgcn_s_waitcnt((T & 15) | (7 << 4) | ((T >> 4) << 14));
+    else
+      __builtin_amdgcn_s_waitcnt(7 << 4);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
 
   f32x16 acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
 
-  auto subtile = [&](const uint16_t* st, int j, int sub) {
-    int t0, t1;
-    tile(j, t0, t1);
-    const int e0 = t0 + 32 * sub, e1 = imin(t1, e0 + 32);
-    if (e0 >= e1) return;
-    const int c = inside(A, e0, e1) + inside(C, e0, e1);
-    const bool full = __all(!valid || (e1 - e0 == 32 && c == 32));
-    if (__all(!valid || c == 0)) return;
+  // S^T and dP^T of one 32-key subtile
+  auto sdp_sub = [&](const uint16_t* st, int sub, f32x16& sv, f32x16& dp) {
     const uint16_t* kr = st + 32 * sub * D + k_row;
     const uint16_t* vr = st + TE + 32 * sub * D + k_row;
-    f32x16 sv{}, dp{};
+    sv = f32x16{};
+    dp = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       const int co = 8 * ((2 * ks + hb) ^ k_swz);
       sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(kr + co), qreg[ks], sv, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vr + co), dreg[ks], dp, 0, 0, 0);
     }
+  };
+  // dS^T of the subtile (keys [e0, e1); every pair allowed when full), then
+  // dQ^T += K^T dS^T
+  auto grad_sub = [&](const uint16_t* st, int sub, int e0, int e1, bool full, const f32x16& sv,
+                      const f32x16& dp) {
     bf16x8 dsb[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -246,22 +256,47 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdArgs a) {
       }
     }
   };
+  // a boundary subtile: classified per wavefront, skipped when no lane sees it
+  auto subtile = [&](const uint16_t* st, int j, int sub) {
+    int t0, t1;
+    tile(j, t0, t1);
+    const int e0 = t0 + 32 * sub, e1 = imin(t1, e0 + 32);
+    if (e0 >= e1) return;
+    const int c = inside(A, e0, e1) + inside(C, e0, e1);
+    const bool full = __all(!valid || (e1 - e0 == 32 && c == 32));
+    if (__all(!valid || c == 0)) return;
+    f32x16 sv, dp;
+    sdp_sub(st, sub, sv, dp);
+    grad_sub(st, sub, e0, e1, full, sv, dp);
+  };
 
   if (nt > 0) {
-    fetch(0);
-    lstore(smem);
-    fetch(1);
-    __syncthreads();
-    int st = 0;
+    // Tile j lives in stage j % NSQ; tile j + 3 goes into the stage of tile
+    // j - 1, which every wavefront finished before the last barrier.
+    auto stq = [&](int j) { return smem + (j % NSQ) * 2 * TE; };
+    int issued = 0;
+    for (; issued < NSQ - 1 && issued < nt; ++issued) issue(issued, stq(issued));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);               // Q, dO and the first tiles
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 #pragma unroll 1
     for (int j = 0; j < nt; ++j) {
-      const uint16_t* cur = smem + st * 2 * TE;
-      subtile(cur, j, 0);
-      subtile(cur, j, 1);
-      lstore(smem + (st ^ 1) * 2 * TE);
-      fetch(j + 2);
-      __syncthreads();
-      st ^= 1;
+      if (issued < nt) issue(issued, stq(issued)), ++issued;
+      const uint16_t* cur = stq(j);
+      if (j < nf) {
+        // clean-prefix tile every row sees: no classification, no branches
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          f32x16 sv, dp;
+          sdp_sub(cur, sub, sv, dp);
+          grad_sub(cur, sub, 0, 0, true, sv, dp);
+        }
+      } else {
+        subtile(cur, j, 0);
+        subtile(cur, j, 1);
+      }
+      settle_for(j + 1, issued);
     }
   }
 
