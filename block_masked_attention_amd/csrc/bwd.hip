@@ -7,9 +7,9 @@
 // per-row log-sum-exp from the forward, for loss = sum(dO * O):
 //   dV = P^T dO,   dP = dO V^T,   dS = P (dP - D),  D_i = sum_c dO_ic O_ic,
 //   dQ = scale dS K,   dK = scale dS^T Q.
-// Three launches:
-//   delta  D per query row (one pass over O and dO).
-//   dq     query-stationary, like the forward: per key tile S^T = K Q^T,
+// Two launches:
+//   dq     query-stationary, like the forward (it also forms D per query row
+//          from O and the dO it holds): per key tile S^T = K Q^T,
 //          dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T (K^T by the LDS
 //          transpose read, dS^T straight from the accumulator registers).
 //   dkdv   key-stationary: a workgroup keeps 128 keys of one (batch, kv
@@ -50,27 +50,6 @@ struct BwdArgs {
 constexpr float kLn2Inv = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
-// D_i = sum_c dO_ic O_ic (fp32), one row per D/8 lanes.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restrict__ o,
-                                                        const uint16_t* __restrict__ dout,
-                                                        float* __restrict__ delta, long long rows) {
-  constexpr int TPR = D / 8;
-  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long row = t / TPR;
-  const int c = (int)(t - row * TPR);
-  float acc = 0.f;
-  if (row < rows) {
-    const u32x4 x = *(const u32x4*)(o + row * D + 8 * c);
-    const u32x4 y = *(const u32x4*)(dout + row * D + 8 * c);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc += bf16_lo(x[e]) * bf16_lo(y[e]) + bf16_hi(x[e]) * bf16_hi(y[e]);
-  }
-#pragma unroll
-  for (int off = TPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && c == 0) delta[row] = acc;
-}
-
 // ---------------------------------------------------------------------------
 // dQ.  One workgroup per (batch, kv head, query tile) as in the forward's
 // training form: NW wavefronts x 32 query slots, half of them on x_t rows
@@ -145,7 +124,23 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdArgs a) {
     }
   }
   const float lse2 = valid ? a.lse[rowi] * kLn2Inv : INFINITY;
-  const float dl = valid ? a.delta[rowi] : 0.f;
+  // D of the slot's row, sum over d of dO O in fp32: lane (ql, hb) holds
+  // d = 16 ks + 8 hb + 0..7 of dO, and the two half-wavefronts add.  The
+  // dK/dV kernel, launched after this one, reads it from the workspace.
+  float dl;
+  {
+    const uint16_t* op = a.o + rowi * D + 8 * hb;
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const u32x4 x = valid ? *(const u32x4*)(op + 16 * ks) : u32x4{0, 0, 0, 0};
+      const u32x4 y = __builtin_bit_cast(u32x4, dreg[ks]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) part += bf16_lo(x[e]) * bf16_lo(y[e]) + bf16_hi(x[e]) * bf16_hi(y[e]);
+    }
+    dl = half_sum(part);
+    if (valid && hb == 0) a.delta[rowi] = dl;
+  }
   Span A{0, 0}, C{0, 0};
   if (valid) row_spans(kHybrid, a.L, 2 * a.L, a.blk, qrow, A, C);
 
@@ -666,12 +661,7 @@ int bwd_make_plan(int B, int Hq, int Hkv, int L, int d, int block, BwdPlan* p, c
 
 template <int D>
 static hipError_t bwd_launch_d(const BwdPlan& p, const BwdArgs& a, hipStream_t st) {
-  const long long rows = (long long)p.B * p.Hq * 2 * p.L;
-  const long long blocks = (rows * (D / 8) + 255) / 256;
-  hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, st, a.o, a.dout, a.delta,
-                     rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
   if (p.nw == 8)
     hipLaunchKernelGGL((bwd_dq_kernel<D, 8>), dim3((unsigned)p.grid_dq), dim3(512), 0, st, a);
   else
