@@ -53,7 +53,8 @@ constexpr float kLn2Inv = 1.4426950408889634f;
 // ---------------------------------------------------------------------------
 // dQ.  One workgroup per (batch, kv head, query tile) as in the forward's
 // training form: NW wavefronts x 32 query slots, half of them on x_t rows
-// and half on the same positions of x_0.
+// and half on the same positions of x_0.  K/V tiles come through a 4-stage
+// DMA ring; the kernel also forms D = rowsum(dO O) of its rows for dK/dV.
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdArgs a) {
   constexpr int KSTEPS = D / 16, DT = D / 32, CPR = D / 8;
