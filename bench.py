@@ -169,9 +169,17 @@ def cpu_baseline_attention(case, budget_s=20.0, min_s=10.0):
         oracle.attention("hybrid", case.q[:nb, :heads], case.k[:nb, :kvh], case.v[:nb, :kvh], L, blk)
         total += time.perf_counter() - t0
         calls += 1
+    # one thread, on one kv head of batch 0 (its G query heads)
+    t0 = time.perf_counter()
+    oracle.attention("hybrid", case.q[:1, :G], case.k[:1, :1], case.v[:1, :1], L, blk, nthreads=1)
+    dt1 = time.perf_counter() - t0
+    flops1 = 4 * d * pairs_per_head * G
     return {"value": flops * calls / total / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
             "cpu": _cpu_model(), "sample": f"all {rows} rows of {heads} query heads ({kvh} kv heads) of {nb} batch(es) "
-                      f"({flops / 1e9:.1f} GFLOP per call, {calls} call(s), {total:.1f} s)"}
+                      f"({flops / 1e9:.1f} GFLOP per call, {calls} call(s), {total:.1f} s)",
+            "single_thread": {"value": flops1 / dt1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                              "sample": f"all {rows} rows of {G} query heads (1 kv head) of batch 0 "
+                                        f"({flops1 / 1e9:.1f} GFLOP, {dt1:.1f} s)"}}
 
 
 def cpu_baseline_commit(logits, masked, tau, k_min, min_s=10.0):
@@ -187,9 +195,14 @@ def cpu_baseline_commit(logits, masked, tau, k_min, min_s=10.0):
         dt += time.perf_counter() - t0
         calls += 1
     committed = int(masked[:g].numpy().sum() - m.sum())
+    t0 = time.perf_counter()
+    oracle.commit(logits[:g], masked[:g].numpy(), tokens, tau, k_min, nthreads=1)
+    dt1 = time.perf_counter() - t0
     return {"value": committed * calls / dt, "unit": "committed tokens/s", "cores": oracle.max_threads(),
             "kind": "oracle", "cpu": _cpu_model(),
-            "sample": f"{g} of {G} groups ({committed} tokens per call, {calls} calls, {dt:.1f} s)"}
+            "sample": f"{g} of {G} groups ({committed} tokens per call, {calls} calls, {dt:.1f} s)",
+            "single_thread": {"value": committed / dt1, "unit": "committed tokens/s", "cores": 1,
+                              "sample": f"{g} of {G} groups, one call ({dt1:.2f} s)"}}
 
 
 def main():
