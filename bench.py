@@ -137,6 +137,33 @@ def _cpu_model():
     return "unknown"
 
 
+def host_threads():
+    """Threads the CPU baseline runs on, and what they were derived from: the
+    CPUs this process may run on (affinity), capped by OMP_NUM_THREADS when
+    it is set (the host's CPU share where the machine is shared)."""
+    nproc = os.cpu_count() or 1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = nproc
+    omp_env = os.environ.get("OMP_NUM_THREADS")
+    threads = affinity
+    try:
+        if omp_env is not None and int(omp_env.split(",")[0]) > 0:
+            threads = min(threads, int(omp_env.split(",")[0]))
+    except ValueError:
+        pass
+    quota = None
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as fh:
+            q, per = fh.read().split()[:2]
+            if q != "max":
+                quota = round(int(q) / int(per), 2)
+    except (OSError, ValueError):
+        pass
+    return threads, {"nproc": nproc, "affinity": affinity, "OMP_NUM_THREADS": omp_env, "cgroup_cpus": quota}
+
+
 def cpu_baseline_attention(case, budget_s=20.0, min_s=10.0):
     """The oracle, untuned, on a bounded sample of the same workload: every
     row of the query heads of the first kv head(s) of batch 0, the number of
@@ -149,11 +176,12 @@ def cpu_baseline_attention(case, budget_s=20.0, min_s=10.0):
     d = case.q.shape[-1]
     G = case.q.shape[1] // case.k.shape[1]
     Hkv, B = case.k.shape[1], case.q.shape[0]
+    nt, host = host_threads()
     kvh, nb = 1, 1
     while True:
         heads = G * kvh
         t0 = time.perf_counter()
-        oracle.attention("hybrid", case.q[:nb, :heads], case.k[:nb, :kvh], case.v[:nb, :kvh], L, blk)
+        oracle.attention("hybrid", case.q[:nb, :heads], case.k[:nb, :kvh], case.v[:nb, :kvh], L, blk, nthreads=nt)
         dt = time.perf_counter() - t0
         flops = 4 * d * pairs_per_head * heads * nb
         if dt > budget_s / 4 or (kvh == Hkv and nb == B):
@@ -166,7 +194,7 @@ def cpu_baseline_attention(case, budget_s=20.0, min_s=10.0):
     calls, total = 1, dt
     while total < min_s:
         t0 = time.perf_counter()
-        oracle.attention("hybrid", case.q[:nb, :heads], case.k[:nb, :kvh], case.v[:nb, :kvh], L, blk)
+        oracle.attention("hybrid", case.q[:nb, :heads], case.k[:nb, :kvh], case.v[:nb, :kvh], L, blk, nthreads=nt)
         total += time.perf_counter() - t0
         calls += 1
     # one thread, on one kv head of batch 0 (its G query heads)
@@ -174,8 +202,8 @@ def cpu_baseline_attention(case, budget_s=20.0, min_s=10.0):
     oracle.attention("hybrid", case.q[:1, :G], case.k[:1, :1], case.v[:1, :1], L, blk, nthreads=1)
     dt1 = time.perf_counter() - t0
     flops1 = 4 * d * pairs_per_head * G
-    return {"value": flops * calls / total / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "cpu": _cpu_model(), "sample": f"all {rows} rows of {heads} query heads ({kvh} kv heads) of {nb} batch(es) "
+    return {"value": flops * calls / total / 1e12, "unit": "TFLOP/s", "cores": nt, "kind": "oracle",
+            "cpu": _cpu_model(), "host": host, "sample": f"all {rows} rows of {heads} query heads ({kvh} kv heads) of {nb} batch(es) "
                       f"({flops / 1e9:.1f} GFLOP per call, {calls} call(s), {total:.1f} s)",
             "single_thread": {"value": flops1 / dt1 / 1e12, "unit": "TFLOP/s", "cores": 1,
                               "sample": f"all {rows} rows of {G} query heads (1 kv head) of batch 0 "
@@ -188,18 +216,19 @@ def cpu_baseline_commit(logits, masked, tau, k_min, min_s=10.0):
     G = logits.shape[0]
     g = G                                   # the whole commit call is well under a minute of CPU work
     tokens = np.full((g, logits.shape[1]), -1, dtype=np.int64)
+    nt, host = host_threads()
     calls, dt = 0, 0.0
     while dt < min_s:                       # the oracle returns new arrays: every call does the whole commit
         t0 = time.perf_counter()
-        _, m, _ = oracle.commit(logits[:g], masked[:g].numpy(), tokens, tau, k_min)
+        _, m, _ = oracle.commit(logits[:g], masked[:g].numpy(), tokens, tau, k_min, nthreads=nt)
         dt += time.perf_counter() - t0
         calls += 1
     committed = int(masked[:g].numpy().sum() - m.sum())
     t0 = time.perf_counter()
     oracle.commit(logits[:g], masked[:g].numpy(), tokens, tau, k_min, nthreads=1)
     dt1 = time.perf_counter() - t0
-    return {"value": committed * calls / dt, "unit": "committed tokens/s", "cores": oracle.max_threads(),
-            "kind": "oracle", "cpu": _cpu_model(),
+    return {"value": committed * calls / dt, "unit": "committed tokens/s", "cores": nt,
+            "kind": "oracle", "cpu": _cpu_model(), "host": host,
             "sample": f"{g} of {G} groups ({committed} tokens per call, {calls} calls, {dt:.1f} s)",
             "single_thread": {"value": committed / dt1, "unit": "committed tokens/s", "cores": 1,
                               "sample": f"{g} of {G} groups, one call ({dt1:.2f} s)"}}
@@ -210,6 +239,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="untimed launches continue for this many seconds after the warm-up steps")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -240,6 +271,17 @@ def main():
     for _ in range(args.warmup):
         bda.attn_fwd(q, k, v, "hybrid", blk, out=out)
     torch.cuda.synchronize()
+    # Settle: the first few dozen launches of a fresh process run up to 30%
+    # slower (clocks still ramping), so untimed launches continue for at
+    # least settle_s seconds of GPU time before the K timed steps.
+    settle_n, t_set = 0, time.perf_counter()
+    while time.perf_counter() - t_set < args.settle_s:
+        for _ in range(10):
+            bda.attn_fwd(q, k, v, "hybrid", blk, out=out)
+        settle_n += 10
+        torch.cuda.synchronize()
+    settle_s = time.perf_counter() - t_set
+    log(f"[bench] settle: {settle_n} untimed launches over {settle_s:.2f} s after {args.warmup} warm-up launches")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
     for _ in range(args.steps):
@@ -265,6 +307,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"launches": settle_n, "seconds": round(settle_s, 3)},
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -46,6 +46,19 @@
 
 enum { OR_HYBRID = 0, OR_DECODE = 1, OR_CAUSAL = 2 };
 
+/* Threads of one call: nthreads when positive, else the OpenMP default.  The
+ * count is given to each parallel region, so a call never changes the
+ * process-wide default that later calls see. */
+static int thread_count(int nthreads)
+{
+#ifdef _OPENMP
+    return nthreads > 0 ? nthreads : omp_get_max_threads();
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
 /* ---------------------------------------------------------------------- */
 /* Mask                                                                     */
 /* ---------------------------------------------------------------------- */
@@ -170,13 +183,9 @@ int oracle_attention(int mode, const float* q, const float* k, const float* v, d
     double scale = 1.0 / sqrt((double)d);
     long group = Hq / Hkv;
     long total = sel ? nsel : B * Hq * rows;
-#ifdef _OPENMP
-    if (nthreads > 0) omp_set_num_threads(nthreads);
-#else
-    (void)nthreads;
-#endif
+    const int nt = thread_count(nthreads);
     int fail = 0;
-#pragma omp parallel
+#pragma omp parallel num_threads(nt)
     {
         double* s = (double*)malloc(sizeof(double) * (size_t)keys);
         if (!s) {
@@ -228,13 +237,9 @@ int oracle_attention_bwd(int mode, const float* q, const float* k, const float* 
     oracle_mask(mode, L, block, M);
     const double scale = 1.0 / sqrt((double)d);
     const long group = Hq / Hkv;
-#ifdef _OPENMP
-    if (nthreads > 0) omp_set_num_threads(nthreads);
-#else
-    (void)nthreads;
-#endif
+    const int nt = thread_count(nthreads);
     int fail = 0;
-#pragma omp parallel
+#pragma omp parallel num_threads(nt)
     {
         double* p = (double*)malloc(sizeof(double) * (size_t)keys);
         double* o = (double*)malloc(sizeof(double) * (size_t)d);
@@ -339,12 +344,8 @@ int oracle_commit(const float* logits, int64_t* tokens, uint8_t* masked, float t
     double* p = (double*)malloc(sizeof(double) * (size_t)(G * R + 1));
     long* a = (long*)malloc(sizeof(long) * (size_t)(G * R + 1));
     if (!p || !a) { free(p); free(a); return 1; }
-#ifdef _OPENMP
-    if (nthreads > 0) omp_set_num_threads(nthreads);
-#else
-    (void)nthreads;
-#endif
-#pragma omp parallel for schedule(dynamic, 1)
+    const int nt = thread_count(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
     for (long t = 0; t < G * R; ++t) {
         p[t] = NAN; a[t] = -1;
         if (!masked[t]) continue;
@@ -415,12 +416,8 @@ int oracle_verify(const float* logits, const int64_t* drafts, int64_t* argmax_ou
                   long B, long R, long V, int nthreads)
 {
     if (B < 0 || R < 0 || V <= 0) return 1;
-#ifdef _OPENMP
-    if (nthreads > 0) omp_set_num_threads(nthreads);
-#else
-    (void)nthreads;
-#endif
-#pragma omp parallel for schedule(dynamic, 1)
+    const int nt = thread_count(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
     for (long t = 0; t < B * R; ++t) {
         const float* row = logits + t * V;
         double m = (double)row[0];
@@ -453,12 +450,8 @@ int oracle_row_stats(const float* logits, const uint8_t* masked, double* conf, i
                      double* entropy, double* mean, long G, long R, long V, int nthreads)
 {
     if (G < 0 || R < 0 || V <= 0) return 1;
-#ifdef _OPENMP
-    if (nthreads > 0) omp_set_num_threads(nthreads);
-#else
-    (void)nthreads;
-#endif
-#pragma omp parallel for schedule(dynamic, 1)
+    const int nt = thread_count(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
     for (long t = 0; t < G * R; ++t) {
         if (masked && !masked[t]) continue;
         const float* row = logits + t * V;
@@ -518,12 +511,8 @@ int oracle_commit_entropy(const float* logits, int64_t* tokens, uint8_t* masked,
                           long k_min, long G, long R, long V, double* entropy, int64_t* argmax, int nthreads)
 {
     if (G < 0 || R < 0 || V <= 0 || k_min < 0 || !(temperature > 0.0)) return 1;
-#ifdef _OPENMP
-    if (nthreads > 0) omp_set_num_threads(nthreads);
-#else
-    (void)nthreads;
-#endif
-#pragma omp parallel for schedule(dynamic, 1)
+    const int nt = thread_count(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
     for (long t = 0; t < G * R; ++t) {
         if (!masked[t]) continue;
         const float* row = logits + t * V;

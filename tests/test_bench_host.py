@@ -50,3 +50,23 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300, cwd=ROOT)
     assert p.returncode != 0
     assert "one GPU" in (p.stdout + p.stderr)
+
+
+def test_single_thread_call_leaves_the_default_thread_count():
+    """A call with nthreads=1 sets the count for its own parallel regions
+    only: the process-wide OpenMP default that later calls see is unchanged."""
+    before = oracle.max_threads()
+    case, logits, masked = synth.tiny()
+    oracle.commit(logits, masked.numpy(), np.full(tuple(masked.shape), -1, dtype=np.int64), 0.85, 1, nthreads=1)
+    oracle.attention("hybrid", case.q, case.k, case.v, case.L, case.block, nthreads=1)
+    assert oracle.max_threads() == before
+
+
+def test_baseline_records_its_thread_count_and_host(monkeypatch):
+    monkeypatch.setenv("OMP_NUM_THREADS", "2")
+    nt, host = bench.host_threads()
+    assert nt == min(2, host["affinity"]) and host["OMP_NUM_THREADS"] == "2"
+    assert host["nproc"] >= host["affinity"] >= 1
+    case, _, _ = synth.tiny()
+    r = bench.cpu_baseline_attention(case, budget_s=0.01, min_s=0.05)
+    assert r["cores"] == nt and r["host"]["affinity"] == host["affinity"]
