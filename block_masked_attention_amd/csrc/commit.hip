@@ -220,14 +220,20 @@ __global__ __launch_bounds__(kCommitThreads) void stream_kernel(const void* __re
     }
     // pass 2: Z (and T) against M; every thread's sums share it, so they add
     float z = 0.f, tt = 0.f;
-    if (KIND != kArgmax) {
+    // A chunk whose values are all -inf (banned tokens) holds no mass: Z = T
+    // = 0, and its maximum -inf loses every merge.
+    if (KIND != kArgmax && M != -INFINITY) {
       const float nb = -M * xs;
       float acc[4] = {0.f, 0.f, 0.f, 0.f}, acct[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int v = 0; v < VPT; ++v)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float u = fmaf(x[v][e], xs, nb);   // (l - M) xs
+          // (l - M) xs.  For T it is clamped at -160: exp2 of anything below
+          // -149 is 0 in fp32 either way, and a -inf logit then adds 0 * -160
+          // instead of 0 * -inf = NaN.
+          float u = fmaf(x[v][e], xs, nb);
+          if (KIND == kWithZT) u = fmaxf(u, -160.f);
           const float p = exp2_fast(u);
           acc[e & 3] += p;
           if (KIND == kWithZT) acct[e & 3] = fmaf(p, u, acct[e & 3]);
