@@ -1,8 +1,7 @@
 """GPU parity of the attention kernels against the fp64 oracle.
 
-Small cases are compared element by element (every output); the full-size
-workloads are compared on sampled rows that the oracle computes one by one,
-in the same launch configuration the benchmark times.
+Every case is compared element by element (every output), the full-size
+workloads included, in the same launch configuration the benchmark times.
 """
 import numpy as np
 import pytest
@@ -10,7 +9,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import ATOL, assert_close_attn, dev, sample_rows, say
+from gpu_util import ATOL, assert_close_attn, dev, say
 
 pytestmark = pytest.mark.gpu
 
@@ -81,44 +80,58 @@ def test_tiny_config_fp32_inputs_rounded():
     assert_close_attn(got.numpy(), ref, "tiny")
 
 
-def _sampled(case, sel, what):
+# Element-wise cases whose persistent walk takes several items per
+# workgroup (the grid is one workgroup per compute unit at d = 128, two at
+# d = 64 and 32), so the DMA ring carried from one item into the next and the
+# boundary tile that ends every item are checked on every output.
+MULTI_ITEM = [
+    # mode, B, Hq, Hkv, L, d, block               items per workgroup (256 CUs)
+    ("hybrid", 4, 32, 8, 1024, 128, 32),         # 1024 items: 4
+    ("hybrid", 4, 32, 8, 2048, 64, 32),          # 2048 items on 512: 4
+    ("hybrid", 4, 32, 8, 1536, 32, 28),          # 1536 items on 512: 3, ragged blocks
+    ("hybrid", 3, 32, 8, 1000, 128, 7),          # ragged tail of the sequence, short blocks
+    ("causal", 2, 32, 8, 2048, 128, 2048),       # prefill form: 512 items, 2
+    ("causal", 4, 32, 8, 2100, 64, 2100),        # prefill, 1056 items on 512, ragged last query tile
+]
+
+
+@pytest.mark.parametrize("mode,B,Hq,Hkv,L,d,blk", MULTI_ITEM)
+def test_multi_item_elementwise(mode, B, Hq, Hkv, L, d, blk):
+    say(f"[attn multi-item] {mode} B={B} Hq={Hq} Hkv={Hkv} L={L} d={d} block={blk}")
+    q, k, v = _case(mode, B, Hq, Hkv, L, d, blk, seed=2000 + L + d + blk)
+    got = _run(mode, q, k, v, blk)
+    ref = oracle.attention(mode, q, k, v, L, blk)
+    assert_close_attn(got.numpy(), ref, f"{mode} B={B} L={L} d={d} b={blk}")
+
+
+def _dense(case, what):
+    """Every output element of a full-size workload against the oracle, in
+    the launch configuration the benchmark times."""
     mode, L, blk = case.mode, case.L, case.block
-    say(f"[attn full] {what}: shapes q={tuple(case.q.shape)} k={tuple(case.k.shape)}")
+    say(f"[attn full dense] {what}: shapes q={tuple(case.q.shape)} k={tuple(case.k.shape)}")
     out = bda.attn_fwd(case.q.to(dev()), case.k.to(dev()), case.v.to(dev()), mode, blk)
     torch.cuda.synchronize()
-    out = out.cpu()
-    got = np.stack([out[b, h, i].float().numpy() for (b, h, i) in sel])
-    ref = oracle.attention(mode, case.q, case.k, case.v, L, blk, sel=sel)
-    return assert_close_attn(got, ref, what)
+    got = out.float().cpu().numpy()
+    del out
+    ref = oracle.attention(mode, case.q, case.k, case.v, L, blk)
+    err = assert_close_attn(got, ref, what)
+    say(f"[attn full dense] {what}: max err {err:.3e}")
 
 
-def test_full_training_form_sampled():
-    case = synth.hybrid_train()
-    B, H, R = case.q.shape[:3]
-    L = case.L
-    must = [(0, 0, 0), (0, 0, L - 1), (0, 0, L), (3, 31, 2 * L - 1), (1, 5, L + 31), (2, 17, 32), (3, 0, L - 32)]
-    _sampled(case, sample_rows(B, H, R, 384, seed=7, must=must), "training form B=4 L=2048 b=32")
+def test_full_training_form_dense():
+    _dense(synth.hybrid_train(), "training form B=4 L=2048 b=32 (every row)")
 
 
-def test_full_decode_sampled():
-    case = synth.decode_block()
-    B, H, R = case.q.shape[:3]
-    must = [(0, 0, r) for r in range(28)] + [(31, 31, r) for r in range(28)]
-    _sampled(case, sample_rows(B, H, R, 200, seed=8, must=must), "decode B=32 n=28 KV=4124")
+def test_full_prefill_dense():
+    _dense(synth.multimodal_prefill(), "prefill B=2 n=L=4096 (every row)")
 
 
-def test_full_verify_sampled():
-    case = synth.verify_block()
-    B, H, R = case.q.shape[:3]
-    must = [(0, 0, r) for r in range(28)] + [(15, 31, r) for r in range(28)]
-    _sampled(case, sample_rows(B, H, R, 200, seed=9, must=must), "verify B=16 n=28 KV=8220")
+def test_full_decode_dense():
+    _dense(synth.decode_block(), "decode B=32 n=28 KV=4124 (every row)")
 
 
-def test_full_prefill_sampled():
-    case = synth.multimodal_prefill()
-    B, H, R = case.q.shape[:3]
-    must = [(0, 0, 0), (0, 0, 1), (1, 31, R - 1), (1, 3, 4095), (0, 8, 2048)]
-    _sampled(case, sample_rows(B, H, R, 256, seed=10, must=must), "prefill B=2 n=L=4096")
+def test_full_verify_dense():
+    _dense(synth.verify_block(), "verify B=16 n=28 KV=8220 (every row)")
 
 
 def test_masked_perturbation_bitwise():
