@@ -40,26 +40,27 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // Written as inline assembly so that the compiler does not pair every later
 // LDS read with a wait for all such loads: the kernel waits for them itself
 // (s_waitcnt vmcnt) before the barrier that publishes a stage.  M0 is set in
-// the same statement and used by nothing else in these kernels.
+// the same statement and named as clobbered, so the compiler keeps nothing
+// of its own there across these loads.
 __device__ __forceinline__ void lds_dma16(const uint16_t* g, const uint16_t* lds_run) {
   const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_run);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(base) : "memory");
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(base) : "memory", "m0");
 }
 // The same with the non-temporal hint, for data read once (streamed caches).
 __device__ __forceinline__ void lds_dma16_nt(const uint16_t* g, const uint16_t* lds_run) {
   const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_run);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(base) : "memory");
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(base) : "memory", "m0");
 }
 
 // The same with the run starting at LDS byte address m0 (uniform).
 __device__ __forceinline__ void lds_dma16s(const uint16_t* g, unsigned m0) {
   m0 = __builtin_amdgcn_readfirstlane(m0);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory");
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
 }
 // 4 bytes per lane: lane i writes LDS byte address m0 + 4*i.
 __device__ __forceinline__ void lds_dma4s(const float* g, unsigned m0) {
   m0 = __builtin_amdgcn_readfirstlane(m0);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory");
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
 }
 
 // ds_read_b64_tr_b16: within each 16-lane group, lane j receives element
