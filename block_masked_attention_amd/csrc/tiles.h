@@ -35,6 +35,13 @@ __device__ __forceinline__ int chunk_off(int r, int c) {  // element offset of c
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
+// M0 is a reserved register to the compiler, which warns when an asm
+// statement names it as clobbered; the clobber is still recorded as a def of
+// M0, which is what keeps any M0 value of the compiler's from being assumed
+// to survive these statements.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+
 // 16 bytes per lane from global memory straight into LDS: lane i of the
 // wavefront writes lds_run + 16*i (lds_run must be the same for every lane).
 // Written as inline assembly so that the compiler does not pair every later
@@ -62,6 +69,8 @@ __device__ __forceinline__ void lds_dma4s(const float* g, unsigned m0) {
   m0 = __builtin_amdgcn_readfirstlane(m0);
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
 }
+
+#pragma clang diagnostic pop
 
 // ds_read_b64_tr_b16: within each 16-lane group, lane j receives element
 // (j & 3) of the 4-element row read by lane 4*e + (j >> 2), for e = 0..3.
