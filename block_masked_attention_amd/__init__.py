@@ -67,6 +67,8 @@ def _load():
     L.bda_attn_workspace_bytes.restype = S
     L.bda_commit.argtypes = [P, I, P, P, F, I, I, I, I, P, S, P]
     L.bda_commit.restype = I
+    L.bda_commit_noalloc.argtypes = [P, I, P, P, F, I, I, I, I, P]
+    L.bda_commit_noalloc.restype = I
     L.bda_commit_workspace_bytes.argtypes = [I, I, I]
     L.bda_commit_workspace_bytes.restype = S
     L.bda_verify.argtypes = [P, I, P, P, P, I, I, I, P, S, P]
@@ -220,6 +222,27 @@ def commit(logits, tokens, masked, threshold: float, k_min: int, workspace=None)
                         G, R, V, _ptr(ws), need, _stream(dev))
     if rc:
         raise BdaError(rc, "bda_commit")
+    return tokens, masked
+
+
+def commit_noalloc(logits, tokens, masked, threshold: float, k_min: int):
+    """bda_commit over the library's static scratch: nothing is allocated
+    (calls on one GPU must not overlap in time)."""
+    if logits.dim() != 3:
+        raise ValueError("logits must be [G, R, V]")
+    G, R, V = logits.shape
+    dt = {torch.bfloat16: BF16, torch.float32: F32}.get(logits.dtype)
+    if dt is None:
+        raise ValueError("logits must be bfloat16 or float32")
+    if tokens.dtype != torch.int64 or masked.dtype != torch.uint8:
+        raise ValueError("tokens int64, masked uint8")
+    if tuple(tokens.shape) != (G, R) or tuple(masked.shape) != (G, R):
+        raise ValueError("tokens/masked must be [G, R]")
+    dev = _check_dev(logits, tokens, masked)
+    rc = lib.bda_commit_noalloc(_ptr(logits), dt, _ptr(tokens), _ptr(masked), float(threshold), int(k_min),
+                                G, R, V, _stream(dev))
+    if rc:
+        raise BdaError(rc, "bda_commit_noalloc")
     return tokens, masked
 
 

@@ -180,6 +180,34 @@ int bda_commit(const void* logits, int dtype, int64_t* tokens, uint8_t* masked, 
   return ok();
 }
 
+static_assert(BDA_COMMIT_NOALLOC_MAX_BYTES == bda::kCommitNoAllocBytes, "static scratch size mismatch");
+
+int bda_commit_noalloc(const void* logits, int dtype, int64_t* tokens, uint8_t* masked, float threshold,
+                       int k_min, int G, int R, int V, void* stream) {
+  if (int e = check_logits(logits, dtype, G, R, V, "G")) return e;
+  if (k_min < 0) return fail(BDA_EINVAL, "k_min must be >= 0");
+  if (isnan(threshold)) return fail(BDA_EINVAL, "threshold is NaN");
+  const size_t rows = (size_t)G * R;
+  if (rows == 0) return ok();
+  if (!tokens || !masked) return fail(BDA_EINVAL, "tokens and masked must be non-NULL");
+  const size_t lbytes = rows * V * (dtype == BDA_BF16 ? 2 : 4);
+  if (overlap(tokens, rows * 8, logits, lbytes) || overlap(masked, rows, logits, lbytes) ||
+      overlap(tokens, rows * 8, masked, rows))
+    return fail(BDA_EINVAL, "tokens, masked and logits must not overlap");
+  bda::CommitPlan p;
+  bda::commit_make_plan(G, R, V, dtype, &p);
+  if (p.ws_bytes > bda::kCommitNoAllocBytes)
+    return fail(BDA_EWORKSPACE, "G x R x V = %d x %d x %d needs %zu bytes of scratch, above the %zu bytes of "
+                "the static scratch; use bda_commit with a workspace", G, R, V, p.ws_bytes,
+                bda::kCommitNoAllocBytes);
+  void* scratch = nullptr;
+  hipError_t e = bda::commit_noalloc_scratch(&scratch);
+  if (e != hipSuccess) return fail(BDA_EHIP, "static scratch address: %s", hipGetErrorString(e));
+  e = bda::commit_launch(p, logits, tokens, masked, threshold, k_min, scratch, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BDA_EHIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 size_t bda_verify_workspace_bytes(int B, int R, int V) { return bda_commit_workspace_bytes(B, R, V); }
 
 size_t bda_commit_entropy_workspace_bytes(int G, int R, int V) { return bda_commit_workspace_bytes(G, R, V); }

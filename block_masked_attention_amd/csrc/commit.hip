@@ -27,6 +27,8 @@
 // H = log Z - T / Z.
 #include <limits.h>
 
+#include <atomic>
+
 #include "common.h"
 #include "internal.h"
 
@@ -805,6 +807,31 @@ hipError_t commit_entropy_launch(const CommitPlan& p, const void* logits, int64_
 }
 
 int commit_entropy_max_rows() { return kEntMaxR; }
+
+// ---- the commit for callers that cannot allocate: its partials and row
+// scratch live in this file-scope array, one copy per GPU, held until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in): each device's address is taken once with
+// hipGetSymbolAddress, with that device current, and kept per device.
+static __device__ __align__(256) unsigned char scratch[kCommitNoAllocBytes];
+
+static std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+hipError_t commit_noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // concurrent first calls on one device store the same address
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 hipError_t adaptive_stop_launch(const int64_t* argmax, int64_t* prev, int32_t* stable, uint8_t* frozen,
                                 const float* mean_entropy, int G, int R, int stability, float conf_thr,

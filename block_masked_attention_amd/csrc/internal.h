@@ -65,6 +65,12 @@ hipError_t bwd_launch(const BwdPlan& p, const void* q, const void* k, const void
                       const void* dout, const float* lse, void* dq, void* dk, void* dv, void* ws,
                       hipStream_t st);
 
+// The commit over the library's static scratch (no allocation anywhere):
+// the scratch's device address on the current device, taken once per device.
+constexpr size_t kCommitNoAllocBytes = (size_t)1 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t commit_noalloc_scratch(void** ptr);
+
 // Entropy-bound commit and adaptive stopping.
 hipError_t commit_entropy_launch(const CommitPlan& p, const void* logits, int64_t* tokens, uint8_t* masked,
                                  float bound, float temperature, int k_min, void* ws, hipStream_t st);

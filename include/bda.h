@@ -164,6 +164,22 @@ int bda_commit(const void* logits, int dtype, int64_t* tokens, uint8_t* masked,
 size_t bda_commit_workspace_bytes(int G, int R, int V);
 
 /*
+ * bda_commit for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and results as bda_commit, with its scratch in a static
+ * array of BDA_COMMIT_NOALLOC_MAX_BYTES bytes that the library holds on each
+ * GPU it runs on until the process ends.  No memory is allocated or freed.
+ * Calls whose bda_commit_workspace_bytes(G, R, V) exceeds that size return
+ * BDA_EWORKSPACE without launching anything (at V = 131072, up to about 7600
+ * rows).  Every call on one GPU shares that GPU's array: calls that overlap
+ * in time on one GPU (other streams, other threads) race and must not be
+ * issued; calls in one stream are ordered and safe.
+ */
+#define BDA_COMMIT_NOALLOC_MAX_BYTES (1u << 20)
+int bda_commit_noalloc(const void* logits, int dtype, int64_t* tokens, uint8_t* masked,
+                       float threshold, int k_min, int G, int R, int V, void* stream);
+
+/*
  * Verify for linear speculative decoding ([NLD-3x] sec. 2).
  * logits [B, R, V] (BDA_BF16 or BDA_F32), drafts [B, R] int64.
  * argmax_out[B, R] int64 = lowest index of each row's largest logit;
