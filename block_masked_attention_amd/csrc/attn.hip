@@ -20,6 +20,7 @@
 //                  4-key transpose reads of a lane pick exactly the keys its
 //                  eight P values belong to, so nothing is shuffled.
 #include <atomic>
+#include <type_traits>
 
 #include "common.h"
 #include "geometry.h"
@@ -29,6 +30,39 @@
 namespace bda {
 
 constexpr int kBN = 64;   // keys per staged tile (two 32-key MFMA subtiles)
+
+template <int S>
+using IC = std::integral_constant<int, S>;
+
+// LDS layout of a staged K (or V) tile of 64 keys x D (16-byte chunks, CPR =
+// D / 8 per key).  Keys are taken in groups of 8: group g = key / 8 starts at
+// byte g * 16 D, and within it chunk c of key r sits at byte (c / 8) * 1024 +
+// 16 * ((8 (c % 8) + ((r % 8) ^ 4 ((c / 2) % 2))) ^ 8 (g % 2)).  Why this
+// form:
+//  * one DMA load (64 lanes x 16 bytes, 1 KB) fills 8 keys x 8 chunks (D >=
+//    64) or 16 keys x 4 chunks (D = 32): every 8 lanes read one whole 128-byte
+//    line of a key row, so a streamed cache line is fetched by one load;
+//  * the K operand read of one k-step (16 keys x one chunk per 16 lanes) and
+//    the V transpose read (4 keys x 4 chunks per 16 lanes, 32 lanes per
+//    clock) each touch 16 distinct 16-byte bank groups of the 64-bank LDS;
+//  * every operand address is a lane constant plus a compile-time offset: the
+//    k-step moves by 512 bytes per pair of k-steps plus a parity (two K base
+//    registers), the 32-column tiles of V^T by 512 bytes, the key subtiles by
+//    whole key groups (two V base registers: a key and the key 8 further).
+template <int D>
+__device__ __forceinline__ constexpr int fwd_off(int r, int c) {   // byte offset of chunk c of key r
+  return (r >> 3) * (16 * D) + (c >> 3) * 1024 +
+         16 * ((8 * (c & 7) + ((r & 7) ^ (4 * ((c >> 1) & 1)))) ^ (8 * ((r >> 3) & 1)));
+}
+// Inverse of fwd_off: the key and chunk whose 16 bytes sit at byte b (a
+// multiple of 16) of a tile.
+template <int D>
+__device__ __forceinline__ void fwd_at(int b, int& r, int& c) {
+  const int g = b / (16 * D), rem = b % (16 * D);
+  const int s = ((rem % 1024) >> 4) ^ (8 * (g & 1));
+  c = 8 * (rem >> 10) + (s >> 3);
+  r = 8 * g + ((s & 7) ^ (4 * (((s >> 3) >> 1) & 1)));
+}
 
 struct AttnArgs {
   const uint16_t* q;
@@ -76,7 +110,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
   constexpr int CU = (TCH + NT - 1) / NT;     // chunks per thread per tile
   constexpr int TE = kBN * D;                 // elements of one K (or V) tile
   constexpr int STAGE = 2 * TE;
+  constexpr int KT = 2 * TE;                  // bytes of one K (or V) tile
   __shared__ __attribute__((aligned(16))) uint16_t smem[STAGES * STAGE];
+  // K tiles of the ring stages first, then the V tiles (all K operand reads
+  // stay below 64 KB of the LDS base, within the reads' immediate offset)
+  char* const sm = reinterpret_cast<char*>(smem);
+  auto kst = [&](int stage) { return sm + stage * KT; };
+  auto vst = [&](int stage) { return sm + (STAGES + stage) * KT; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -210,19 +250,19 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
     }
   };
 
-  // lane-constant LDS offsets (elements, within a stage)
-  const int k_row = ql * D;
-  const int k_swz = swz<D>(ql) & (CPR - 1);   // rows 32*sub + ql share it
-  int v_lo[DT], v_hi[DT];                       // keys 4*hb + j/4 and 8 further
+  // Lane-constant LDS byte offsets of the operand reads (fwd_off).  K: key
+  // 32 sub + ql, chunk 2 ks + hb, at kl[ks % 2] + 256 (ks - ks % 2) + 64 D
+  // sub.  V^T: lane (gi = lane / 16, j = lane % 16) reads 4 values at column
+  // 32 dt + 16 (gi % 2) + 4 (j % 4) of key 32 sub + 16 kk + 4 hb + j / 4
+  // (lo) and of the key 8 further (hi), at vl (vh) + 512 dt + 32 D (2 sub +
+  // kk).
+  const int kl0 = fwd_off<D>(ql, hb), kl1 = fwd_off<D>(ql, 2 + hb);
+  int vl, vh;
   {
     const int j = lane & 15, gi = lane >> 4;
-    const int r = 4 * hb + (j >> 2);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int dcol = 32 * dt + 16 * (gi & 1) + 4 * (j & 3);
-      v_lo[dt] = chunk_off<D>(r, dcol >> 3) + (dcol & 7);
-      v_hi[dt] = chunk_off<D>(r + 8, dcol >> 3) + (dcol & 7);
-    }
+    const int r = 4 * hb + (j >> 2), c = 2 * (gi & 1) + ((j & 3) >> 1);
+    vl = fwd_off<D>(r, c) + 8 * (j & 1);
+    vh = fwd_off<D>(r + 8, c) + 8 * (j & 1);
   }
 
   u32x4 kreg[CU], vreg[CU];
@@ -240,25 +280,25 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       }
     }
   };
-  auto lstore = [&](uint16_t* st) {
+  auto lstore = [&](int stage) {
 #pragma unroll
     for (int j = 0; j < CU; ++j) {
       const int ch = tid + j * NT;
       if (TCH % NT == 0 || ch < TCH) {
-        const int off = chunk_off<D>(ch / CPR, ch % CPR);
-        *(u32x4*)(st + off) = kreg[j];
-        *(u32x4*)(st + TE + off) = vreg[j];
+        const int off = fwd_off<D>(ch / CPR, ch % CPR);
+        *(u32x4*)(kst(stage) + off) = kreg[j];
+        *(u32x4*)(vst(stage) + off) = vreg[j];
       }
     }
   };
   // S^T = K Q^T for one 32-key subtile of a stage, all column blocks
-  auto qk_sub = [&](const uint16_t* st, int sub, f32x16 (&s)[NQB]) {
+  auto qk_sub = [&](int stage, int sub, f32x16 (&s)[NQB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) s[qb] = f32x16{};
-    const uint16_t* kr = st + 32 * sub * D + k_row;
+    const char* kr = kst(stage) + sub * 64 * D;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      const bf16x8 kop = *(const bf16x8*)(kr + 8 * ((2 * ks + hb) ^ k_swz));
+      const bf16x8 kop = *(const bf16x8*)(kr + 256 * (ks & ~1) + ((ks & 1) ? kl1 : kl0));
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
         s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[qb][ks], s[qb], 0, 0, 0);
@@ -266,14 +306,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
   };
   f32x16 o[NQB][DT];
   // O^T += V^T P^T for one 32-key subtile (two 16-key MFMA k-steps)
-  auto pv_sub = [&](const uint16_t* st, int sub, const bf16x8 (&pb)[NQB][2]) {
+  auto pv_sub = [&](int stage, int sub, const bf16x8 (&pb)[NQB][2]) __attribute__((always_inline)) {
+    // the two lane bases of this stage, formed once; every read of the
+    // subtile is one of them plus an immediate offset
+    unsigned b_lo = lds_addr(vst(stage)) + vl, b_hi = lds_addr(vst(stage)) + vh;
+    asm volatile("" : "+v"(b_lo), "+v"(b_hi));
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const uint16_t* vt = st + TE + 16 * (2 * sub + kk) * D;
+      const unsigned vt = (2 * sub + kk) * 32 * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const s16x4 lo = lds_read_tr(vt + v_lo[dt]);
-        const s16x4 hi = lds_read_tr(vt + v_hi[dt]);
+        const s16x4 lo = lds_read_tr_at(b_lo + vt + dt * 512);
+        const s16x4 hi = lds_read_tr_at(b_hi + vt + dt * 512);
         const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
@@ -406,37 +450,65 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
     tile(j, t0, t1);
     gload(t0, t1);
   };
-  // Tile j straight from global memory into an LDS stage (no registers):
-  // each lane of a wavefront's load lands 16 bytes at its lane slot of a
-  // contiguous 1 KB run, so the lane picks the global chunk that the
-  // permuted layout puts there.
+  // Tile [t0, t1) of pair straight from global memory into an LDS stage (no
+  // registers).  Wavefront w loads the 1 KB runs w*DJ + q of the K and of the
+  // V tile; lane i of a run fills bytes 1024 run + 16 i of the stage, so it
+  // loads the key and chunk that fwd_at names there.  The source is the
+  // tile's first key row (a uniform base, in SGPRs) plus a 32-bit lane
+  // offset; in a short tile, keys past t1 - 1 repeat key t1 - 1 (finite data
+  // that the masks never let through).
   constexpr int DJ = TCH >= NT ? TCH / NT : 1;   // DMA loads per wavefront per matrix
-  auto dma_keys = [&](int pair, int t0, int t1, uint16_t* st) {
-    const uint16_t* kb = a.k + (size_t)pair * a.Sk * D;
-    const uint16_t* vb = a.v + (size_t)pair * a.Sk * D;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  int d_row[DJ];
+  unsigned d_off[DJ];
 #pragma unroll
-    for (int q = 0; q < DJ; ++q) {
-      const int run = w * DJ + q;                 // 64-chunk run of the tile
-      if (run * 64 < TCH) {
-        const int pos = run * 64 + lane;
-        const int r = pos / CPR, pc = pos % CPR;
-        const int c = pc ^ (swz<D>(r) & (CPR - 1));
-        const size_t off = (size_t)imin(t0 + r, t1 - 1) * D + 8 * c;
-        const uint16_t* dst = st + run * 64 * 8;
-        if constexpr (KS) {   // each key is read once per item
-          lds_dma16_nt(kb + off, dst);
-          lds_dma16_nt(vb + off, dst + TE);
-        } else {
-          lds_dma16(kb + off, dst);
-          lds_dma16(vb + off, dst + TE);
+  for (int q = 0; q < DJ; ++q) {
+    int r, c;
+    fwd_at<D>(1024 * (w * DJ + q) + 16 * lane, r, c);
+    d_row[q] = r;
+    d_off[q] = (unsigned)(r * 2 * D + c * 16);
+  }
+  auto dma_keys = [&](int pair, int t0, int t1, int stage) __attribute__((always_inline)) {
+    const size_t row0 = ((size_t)pair * a.Sk + t0) * D;
+    const uint16_t* kb = a.k + row0;
+    const uint16_t* vb = a.v + row0;
+    const unsigned mk = (unsigned)(uintptr_t)kst(stage), mv = (unsigned)(uintptr_t)vst(stage);
+    if (t1 - t0 == kBN) {
+#pragma unroll
+      for (int q = 0; q < DJ; ++q) {
+        const int run = wu * DJ + q;
+        if (run * 64 < TCH) {
+          if constexpr (KS) {   // each key is read once per item
+            lds_dma16_sa_nt(kb, d_off[q], mk + run * 1024);
+            lds_dma16_sa_nt(vb, d_off[q], mv + run * 1024);
+          } else {
+            lds_dma16_sa(kb, d_off[q], mk + run * 1024);
+            lds_dma16_sa(vb, d_off[q], mv + run * 1024);
+          }
+        }
+      }
+    } else {
+      const int last = t1 - 1 - t0;
+#pragma unroll
+      for (int q = 0; q < DJ; ++q) {
+        const int run = wu * DJ + q;
+        if (run * 64 < TCH) {
+          const unsigned off = d_off[q] - (unsigned)((d_row[q] - imin(d_row[q], last)) * 2 * D);
+          if constexpr (KS) {
+            lds_dma16_sa_nt(kb, off, mk + run * 1024);
+            lds_dma16_sa_nt(vb, off, mv + run * 1024);
+          } else {
+            lds_dma16_sa(kb, off, mk + run * 1024);
+            lds_dma16_sa(vb, off, mv + run * 1024);
+          }
         }
       }
     }
   };
-  auto dma = [&](const Geom& gm, int j, uint16_t* st) {
+  auto dma = [&](const Geom& gm, int j, int stage) __attribute__((always_inline)) {
     int t0, t1;
     tile_in(gm, j, t0, t1);
-    dma_keys(gm.pair, t0, t1, st);
+    dma_keys(gm.pair, t0, t1, stage);
   };
   // All but the newest tile's DMA loads (and every LDS access) have landed;
   // then the workgroup barrier (without the fence of __syncthreads, which
@@ -458,7 +530,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
     asm volatile("" ::: "memory");
   };
   // boundary tile j held in stage st: per-wavefront FULL / EMPTY / PARTIAL
-  auto slow_tile = [&](const uint16_t* st, int j) {
+  auto slow_tile = [&](int st, int j) {
     int t0, t1;
     tile(j, t0, t1);
     Span A[NQB], C[NQB];
@@ -552,13 +624,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
     const int nf = cur.nf, nt = cur.nt;
     if (nt > 0) {
       fetch(0);
-      lstore(smem);
+      lstore(0);
       fetch(1);
       __syncthreads();
       int st = 0;
 #pragma unroll 1
       for (int i = 0; i < nf; ++i) {
-        const uint16_t* cu = smem + st * STAGE;
+        const int cu = st;
         f32x16 sa[NQB], sb[NQB];
         bf16x8 pb[NQB][2];
         qk_sub(cu, 0, sa);
@@ -567,15 +639,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
         pv_sub(cu, 0, pb);
         softmax_fast(sb, pb);
         pv_sub(cu, 1, pb);
-        lstore(smem + (st ^ 1) * STAGE);
+        lstore(st ^ 1);
         fetch(i + 2);
         __syncthreads();
         st ^= 1;
       }
 #pragma unroll 1
       for (int i = nf; i < nt; ++i) {
-        slow_tile(smem + st * STAGE, i);
-        lstore(smem + (st ^ 1) * STAGE);
+        slow_tile(st, i);
+        lstore(st ^ 1);
         fetch(i + 2);
         __syncthreads();
         st ^= 1;
@@ -590,7 +662,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
     begin_item(blockIdx.x);
     reset_acc();
     const int nf = cur.nf, nt = cur.nt;
-    auto stq = [&](int j) { return smem + (j % STAGES) * STAGE; };
+    auto stq = [&](int j) { return j % STAGES; };
     // Tile j visible to every wavefront, given that tiles 0 .. issued-1 have
     // been issued: the (up to three) tiles issued after j stay in flight.
     auto settle_for = [&](int j, int issued) {
@@ -703,14 +775,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
     // geometry), fast steps are always followed by at least one more issued
     // tile, and a boundary step that finds the stream exhausted waits for
     // every load before it reads its tile.
-    auto c_issue = [&](uint16_t* st) -> bool {
+    auto c_issue = [&](int st) __attribute__((always_inline)) -> bool {
       if (!c_live) return false;
       dma(cg, c_j, st);
       if (++c_j == cg.nt) c_next_item();
       return true;
     };
     int sp = 0;   // stream position of the current item's first tile
-    auto stg = [&](int i) { return smem + ((sp + i) & 3) * STAGE; };
+    auto stg = [&](int i) { return (sp + i) & 3; };
     c_issue(stg(0));
     c_issue(stg(1));
     c_issue(stg(2));
@@ -737,7 +809,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
         if (nf > 0) qk_sub(stg(0), 0, sa);
 #pragma unroll 1
         for (int i = 0; i < nf; ++i) {
-          const uint16_t* cu = stg(i);
+          const int cu = stg(i);
           c_issue(stg(i + 3));
           bf16x8 pb[NQB][2];
           qk_sub(cu, 1, sb);

@@ -70,6 +70,22 @@ __device__ __forceinline__ void lds_dma4s(const float* g, unsigned m0) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
 }
 
+// 16 bytes per lane from base + off (base uniform, in SGPRs; off a 32-bit
+// lane offset) into LDS: lane i writes LDS byte address m0 + 16 i (m0
+// uniform).  The scalar base keeps the per-lane address arithmetic out of
+// the vector unit.
+__device__ __forceinline__ void lds_dma16_sa(const void* base, unsigned off, unsigned m0) {
+  m0 = __builtin_amdgcn_readfirstlane(m0);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(m0)
+               : "memory", "m0");
+}
+// The same with the non-temporal hint.
+__device__ __forceinline__ void lds_dma16_sa_nt(const void* base, unsigned off, unsigned m0) {
+  m0 = __builtin_amdgcn_readfirstlane(m0);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(off), "s"(base), "s"(m0)
+               : "memory", "m0");
+}
+
 #pragma clang diagnostic pop
 
 // ds_read_b64_tr_b16: within each 16-lane group, lane j receives element
@@ -77,5 +93,13 @@ __device__ __forceinline__ void lds_dma4s(const float* g, unsigned m0) {
 __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
+
+// The same at LDS byte address a (an integer, so that an offset added to a
+// base register folds into the instruction's immediate).
+__device__ __forceinline__ s16x4 lds_read_tr_at(unsigned a) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(size_t)a);
+}
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ unsigned lds_addr(const void* p) { return (unsigned)(uintptr_t)p; }
 
 }  // namespace bda
