@@ -326,6 +326,48 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
     }
   };
 
+  // The same two products with their LDS operand reads split off, so the
+  // fast walk can issue the reads of a subtile well before its MFMAs (and
+  // the V reads ahead of the softmax they do not depend on).
+  auto k_load = [&](int stage, int sub, bf16x8 (&kop)[KSTEPS]) __attribute__((always_inline)) {
+    const char* kr = kst(stage) + sub * 64 * D;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      kop[ks] = *(const bf16x8*)(kr + 256 * (ks & ~1) + ((ks & 1) ? kl1 : kl0));
+  };
+  auto qk_mma = [&](const bf16x8 (&kop)[KSTEPS], f32x16 (&s)[NQB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) s[qb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qreg[qb][ks], s[qb], 0, 0, 0);
+  };
+  auto v_load = [&](int stage, int sub, bf16x8 (&vop)[2][DT]) __attribute__((always_inline)) {
+    unsigned b_lo = lds_addr(vst(stage)) + vl, b_hi = lds_addr(vst(stage)) + vh;
+    asm volatile("" : "+v"(b_lo), "+v"(b_hi));
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const unsigned vt = (2 * sub + kk) * 32 * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const s16x4 lo = lds_read_tr_at(b_lo + vt + dt * 512);
+        const s16x4 hi = lds_read_tr_at(b_hi + vt + dt * 512);
+        vop[kk][dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    }
+  };
+  auto pv_mma = [&](const bf16x8 (&vop)[2][DT], const bf16x8 (&pb)[NQB][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+          o[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[kk][dt], pb[qb][kk], o[qb][dt], 0, 0, 0);
+  };
+
   const float sl2 = a.sl2;
   const float thr = 8.f / sl2;   // keep the running max until scores exceed it by 2^8 in weight
   float m_run[NQB], l_run[NQB];
@@ -377,36 +419,41 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
   // weight may then exceed 2^8, or the max is still unset) the running max
   // moves to the subtile's max, O and l are scaled by alpha <= 1 and the
   // subtile is redone with every weight <= 1.  Usually no max is taken.
-  auto softmax_fast = [&](const f32x16 (&s)[NQB], bf16x8 (&pb)[NQB][2]) {
-    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  // expo_fast is the branch-free part, fix_fast the check, the rare redo and
+  // the update of l.
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  auto expo = [&](const f32x16 (&s)[NQB], bf16x8 (&pb)[NQB][2], float (&ls)[NQB], int qb, float nb)
+      __attribute__((always_inline)) {
     const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
-    float ls[NQB];
-    auto expo = [&](int qb, float nb) {
-      float l0 = 0.f, l1 = 0.f;
+    float l0 = 0.f, l1 = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        u32x4 pk;
+    for (int kk = 0; kk < 2; ++kk) {
+      u32x4 pk;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = exp2_fast(fmaf(s[qb][8 * kk + 2 * e], sl2, nb));
-          const float p1 = exp2_fast(fmaf(s[qb][8 * kk + 2 * e + 1], sl2, nb));
-          // Summed from this temporary: reading the pair back out of pk[e]
-          // for the dot product is miscompiled by this toolchain.
-          const unsigned pw = pack_bf16x2(p0, p1);
-          pk[e] = pw;
-          if (e & 1) l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw), one2, l1, false);
-          else l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw), one2, l0, false);
-        }
-        pb[qb][kk] = __builtin_bit_cast(bf16x8, pk);
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = exp2_fast(fmaf(s[qb][8 * kk + 2 * e], sl2, nb));
+        const float p1 = exp2_fast(fmaf(s[qb][8 * kk + 2 * e + 1], sl2, nb));
+        // Summed from this temporary: reading the pair back out of pk[e]
+        // for the dot product is miscompiled by this toolchain.
+        const unsigned pw = pack_bf16x2(p0, p1);
+        pk[e] = pw;
+        if (e & 1) l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw), one2, l1, false);
+        else l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw), one2, l0, false);
       }
-      ls[qb] = l0 + l1;
-    };
+      pb[qb][kk] = __builtin_bit_cast(bf16x8, pk);
+    }
+    ls[qb] = l0 + l1;
+  };
+  auto expo_fast = [&](const f32x16 (&s)[NQB], bf16x8 (&pb)[NQB][2], float (&ls)[NQB])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) expo(s, pb, ls, qb, -m_run[qb] * sl2);
+  };
+  auto fix_fast = [&](const f32x16 (&s)[NQB], bf16x8 (&pb)[NQB][2], float (&ls)[NQB])
+      __attribute__((always_inline)) {
     bool bad = false;
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      expo(qb, -m_run[qb] * sl2);
-      bad |= !(ls[qb] < 256.f);
-    }
+    for (int qb = 0; qb < NQB; ++qb) bad |= !(ls[qb] < 256.f);
     if (__builtin_expect(__any(bad), 0)) {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
@@ -415,7 +462,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
         for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[qb][i]);
         const float m_use = fmaxf(m_run[qb], half_max(mt));
         const float alpha = exp2_fast((m_run[qb] - m_use) * sl2);   // 0 while the max is unset
-        expo(qb, -m_use * sl2);
+        expo(s, pb, ls, qb, -m_use * sl2);
         m_run[qb] = m_use;
         l_run[qb] *= alpha;
 #pragma unroll
@@ -424,6 +471,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
     }
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) l_run[qb] += ls[qb];
+  };
+  auto softmax_fast = [&](const f32x16 (&s)[NQB], bf16x8 (&pb)[NQB][2]) __attribute__((always_inline)) {
+    float ls[NQB];
+    expo_fast(s, pb, ls);
+    fix_fast(s, pb, ls);
   };
   // Keep the softmax of a subtile where it is written, so its exponentials
   // overlap the score MFMAs issued before it instead of being sunk into the
@@ -807,19 +859,74 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
         // so the fast body has no branch besides the rare rescale.
         f32x16 sa[NQB], sb[NQB];
         if (nf > 0) qk_sub(stg(0), 0, sa);
+        // One half step, in a fixed instruction order: the K reads of the
+        // next subtile; then per k-step its score MFMA (into sn), one pair of
+        // exponentials of the current subtile's softmax (sc) and two of the
+        // current subtile's V reads (independent of its softmax); then the
+        // softmax check and the P V MFMAs.  The scheduling fences keep that
+        // order, so every wavefront issues exponentials while its own score
+        // MFMAs run.
+        auto half_step = [&](int kstage, int ksub, int vstage, int vsub, f32x16 (&sn)[NQB],
+                             const f32x16 (&sc)[NQB]) __attribute__((always_inline)) {
+          constexpr int PP = 8 * NQB / KSTEPS;     // exponential pairs per k-step
+          constexpr int VR = 2 * DT;              // V^T operands of a subtile
+          bf16x8 kop[KSTEPS], vop[2][DT], pb[NQB][2];
+          u32x4 pk[NQB][2];
+          float l0[NQB], l1[NQB], nb[NQB], ls[NQB];
+          k_load(kstage, ksub, kop);
+          unsigned b_lo = lds_addr(vst(vstage)) + vl, b_hi = lds_addr(vst(vstage)) + vh;
+          asm volatile("" : "+v"(b_lo), "+v"(b_hi));
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) {
+            nb[qb] = -m_run[qb] * sl2;
+            l0[qb] = 0.f;
+            l1[qb] = 0.f;
+            sn[qb] = f32x16{};
+          }
+          typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+          const bf16x2_t one2 = {(__bf16)1.f, (__bf16)1.f};
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb)
+              sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qreg[qb][ks], sn[qb], 0, 0, 0);
+#pragma unroll
+            for (int t = ks * PP; t < (ks + 1) * PP; ++t) {
+              const int qb = t / 8, kk = (t % 8) / 4, e = t % 4;
+              const float p0 = exp2_fast(fmaf(sc[qb][8 * kk + 2 * e], sl2, nb[qb]));
+              const float p1 = exp2_fast(fmaf(sc[qb][8 * kk + 2 * e + 1], sl2, nb[qb]));
+              // summed from this temporary (see softmax_fast)
+              const unsigned pw = pack_bf16x2(p0, p1);
+              pk[qb][kk][e] = pw;
+              if (e & 1) l1[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw), one2, l1[qb], false);
+              else l0[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw), one2, l0[qb], false);
+            }
+#pragma unroll
+            for (int v = ks * VR / KSTEPS; v < (ks + 1) * VR / KSTEPS; ++v) {
+              const int kk = v / DT, dt = v % DT;
+              const unsigned vt = (2 * vsub + kk) * 32 * D + dt * 512;
+              const s16x4 lo = lds_read_tr_at(b_lo + vt);
+              const s16x4 hi = lds_read_tr_at(b_hi + vt);
+              vop[kk][dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) {
+            pb[qb][0] = __builtin_bit_cast(bf16x8, pk[qb][0]);
+            pb[qb][1] = __builtin_bit_cast(bf16x8, pk[qb][1]);
+            ls[qb] = l0[qb] + l1[qb];
+          }
+          fix_fast(sc, pb, ls);
+          pv_mma(vop, pb);
+        };
 #pragma unroll 1
         for (int i = 0; i < nf; ++i) {
           const int cu = stg(i);
           c_issue(stg(i + 3));
-          bf16x8 pb[NQB][2];
-          qk_sub(cu, 1, sb);
-          softmax_fast(sa, pb);
-          pin(pb);
-          pv_sub(cu, 0, pb);
-          qk_sub(stg(i + 1), 0, sa);
-          softmax_fast(sb, pb);
-          pin(pb);
-          pv_sub(cu, 1, pb);
+          half_step(cu, 1, cu, 0, sb, sa);
+          half_step(stg(i + 1), 0, cu, 1, sa, sb);
           settle();
         }
 #pragma unroll 1
