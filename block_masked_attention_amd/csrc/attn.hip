@@ -510,6 +510,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
   // offset; in a short tile, keys past t1 - 1 repeat key t1 - 1 (finite data
   // that the masks never let through).
   constexpr int DJ = TCH >= NT ? TCH / NT : 1;   // DMA loads per wavefront per matrix
+  constexpr bool ALL_RUNS = TCH / 64 >= NW * DJ;   // every wavefront loads DJ runs (D >= 64)
   const int wu = __builtin_amdgcn_readfirstlane(w);
   int d_row[DJ];
   unsigned d_off[DJ];
@@ -520,16 +521,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
     d_row[q] = r;
     d_off[q] = (unsigned)(r * 2 * D + c * 16);
   }
-  auto dma_keys = [&](int pair, int t0, int t1, int stage) __attribute__((always_inline)) {
-    const size_t row0 = ((size_t)pair * a.Sk + t0) * D;
-    const uint16_t* kb = a.k + row0;
-    const uint16_t* vb = a.v + row0;
+  // n = keys of the tile (1..64) starting at kb / vb
+  auto dma_at = [&](const uint16_t* kb, const uint16_t* vb, int n, int stage) __attribute__((always_inline)) {
     const unsigned mk = (unsigned)(uintptr_t)kst(stage), mv = (unsigned)(uintptr_t)vst(stage);
-    if (t1 - t0 == kBN) {
+    if (n == kBN) {
 #pragma unroll
       for (int q = 0; q < DJ; ++q) {
         const int run = wu * DJ + q;
-        if (run * 64 < TCH) {
+        if (ALL_RUNS || run * 64 < TCH) {
           if constexpr (KS) {   // each key is read once per item
             lds_dma16_sa_nt(kb, d_off[q], mk + run * 1024);
             lds_dma16_sa_nt(vb, d_off[q], mv + run * 1024);
@@ -540,11 +539,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
         }
       }
     } else {
-      const int last = t1 - 1 - t0;
+      const int last = n - 1;
 #pragma unroll
       for (int q = 0; q < DJ; ++q) {
         const int run = wu * DJ + q;
-        if (run * 64 < TCH) {
+        if (ALL_RUNS || run * 64 < TCH) {
           const unsigned off = d_off[q] - (unsigned)((d_row[q] - imin(d_row[q], last)) * 2 * D);
           if constexpr (KS) {
             lds_dma16_sa_nt(kb, off, mk + run * 1024);
@@ -556,6 +555,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
         }
       }
     }
+  };
+  auto dma_keys = [&](int pair, int t0, int t1, int stage) __attribute__((always_inline)) {
+    const size_t row0 = ((size_t)pair * a.Sk + t0) * D;
+    dma_at(a.k + row0, a.v + row0, t1 - t0, stage);
   };
   auto dma = [&](const Geom& gm, int j, int stage) __attribute__((always_inline)) {
     int t0, t1;
@@ -804,11 +807,37 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       const int i = r * GR + ((r & 1) ? GR - 1 - wg : wg);
       return i < a.n_items ? i : -1;
     };
-    // prefetch cursor: tile c_j of item round c_r (geometry cg)
+    // Prefetch cursor: the next tile of the DMA stream, [c_t0, min(c_t0 + 64,
+    // c_hi)) of key range c_reg (0: F, 1: R1, 2: R2) of item round c_r
+    // (geometry cg), kept as a running key position so that a tile costs a
+    // few scalar adds; c_kv is the byte offset of key c_t0 in the K (and V)
+    // tensor.
     Geom cg{};
-    int c_r = -1, c_j = 0;
+    int c_r = -1, c_reg = 0, c_t0 = 0, c_hi = 0;
+    size_t c_kv = 0;
     bool c_live = true;
-    auto c_next_item = [&]() {
+    // Moves to the first non-empty range at or after c_reg; false past R2.
+    auto c_set = [&](const Span& sr) __attribute__((always_inline)) {
+      c_t0 = sr.lo;
+      c_hi = sr.hi;
+      c_kv = ((size_t)cg.pair * a.Sk + c_t0) * (2 * D);
+    };
+    auto c_range = [&]() __attribute__((always_inline)) -> bool {
+      if (c_reg == 0) {
+        if (cg.F.hi > cg.F.lo) return c_set(cg.F), true;
+        c_reg = 1;
+      }
+      if (c_reg == 1) {
+        if (cg.R1.hi > cg.R1.lo) return c_set(cg.R1), true;
+        c_reg = 2;
+      }
+      if (c_reg == 2) {
+        if (cg.R2.hi > cg.R2.lo) return c_set(cg.R2), true;
+        c_reg = 3;
+      }
+      return false;
+    };
+    auto c_next_item = [&]() __attribute__((always_inline)) {
       for (;;) {
         const int idx = item_of(++c_r);
         if (idx < 0) {
@@ -816,8 +845,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
           return;
         }
         geom(idx, cg);
-        c_j = 0;
-        if (cg.nt > 0) return;
+        c_reg = 0;
+        if (cg.nt > 0 && c_range()) return;
       }
     };
     c_next_item();
@@ -829,8 +858,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
     // every load before it reads its tile.
     auto c_issue = [&](int st) __attribute__((always_inline)) -> bool {
       if (!c_live) return false;
-      dma(cg, c_j, st);
-      if (++c_j == cg.nt) c_next_item();
+      const int t1 = imin(c_hi, c_t0 + kBN);
+      dma_at(a.k + c_kv / 2, a.v + c_kv / 2, t1 - c_t0, st);
+      c_t0 += kBN;
+      c_kv += (size_t)kBN * 2 * D;
+      if (__builtin_expect(c_t0 >= c_hi, 0)) {
+        ++c_reg;
+        if (!c_range()) c_next_item();
+      }
       return true;
     };
     int sp = 0;   // stream position of the current item's first tile
