@@ -23,71 +23,24 @@
 #include <type_traits>
 
 #include "common.h"
+#include "attn_index.h"
 #include "geometry.h"
 #include "internal.h"
 #include "tiles.h"
 
 namespace bda {
 
-constexpr int kBN = 64;   // keys per staged tile (two 32-key MFMA subtiles)
-
-template <int S>
-using IC = std::integral_constant<int, S>;
-
-// LDS layout of a staged K (or V) tile of 64 keys x D (16-byte chunks, CPR =
-// D / 8 per key).  Keys are taken in groups of 8: group g = key / 8 starts at
-// byte g * 16 D, and within it chunk c of key r sits at byte (c / 8) * 1024 +
-// 16 * ((8 (c % 8) + ((r % 8) ^ 4 ((c / 2) % 2))) ^ 8 (g % 2)).  Why this
-// form:
-//  * one DMA load (64 lanes x 16 bytes, 1 KB) fills 8 keys x 8 chunks (D >=
-//    64) or 16 keys x 4 chunks (D = 32): every 8 lanes read one whole 128-byte
-//    line of a key row, so a streamed cache line is fetched by one load;
-//  * the K operand read of one k-step (16 keys x one chunk per 16 lanes) and
-//    the V transpose read (4 keys x 4 chunks per 16 lanes, 32 lanes per
-//    clock) each touch 16 distinct 16-byte bank groups of the 64-bank LDS;
-//  * every operand address is a lane constant plus a compile-time offset: the
-//    k-step moves by 512 bytes per pair of k-steps plus a parity (two K base
-//    registers), the 32-column tiles of V^T by 512 bytes, the key subtiles by
-//    whole key groups (two V base registers: a key and the key 8 further).
-template <int D>
-__device__ __forceinline__ constexpr int fwd_off(int r, int c) {   // byte offset of chunk c of key r
-  return (r >> 3) * (16 * D) + (c >> 3) * 1024 +
-         16 * ((8 * (c & 7) + ((r & 7) ^ (4 * ((c >> 1) & 1)))) ^ (8 * ((r >> 3) & 1)));
-}
-// Inverse of fwd_off: the key and chunk whose 16 bytes sit at byte b (a
-// multiple of 16) of a tile.
-template <int D>
-__device__ __forceinline__ void fwd_at(int b, int& r, int& c) {
-  const int g = b / (16 * D), rem = b % (16 * D);
-  const int s = ((rem % 1024) >> 4) ^ (8 * (g & 1));
-  c = 8 * (rem >> 10) + (s >> 3);
-  r = 8 * g + ((s & 7) ^ (4 * (((s >> 3) >> 1) & 1)));
-}
-
-struct AttnArgs {
+struct AttnArgs : AttnIndex {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
   uint16_t* out;
   float* part_o;    // [split][B*Hq*n][D] unnormalised partial outputs
   float* part_ml;   // [split][B*Hq*n][2] (running max in log2 units, row sum)
-  int B, Hq, Hkv, G, mode, L, n, blk, Sq, Sk;
-  int rows_per_wg, n_qtiles, n_splits, split_keys, pairs_per_xcd;
-  int n_items;      // work items (batch x kv head x query tile x key split)
   float sl2;        // log2(e) / sqrt(D)
   const int32_t* kv_len;   // optional [B] (DECODE/CAUSAL): keys of each batch row, clamped to [n, L]
   float* lse;       // optional [B*Hq*Sq]: natural-log log-sum-exp of each row's scores
 };
-
-// Geometry of one work item: its (batch, kv head) pair, query tile and key
-// split, and the key ranges its rows need (see the kernel).
-struct Geom {
-  Span F, R1, R2;
-  int nf, n1, nt;
-  int pair, qt, split;
-  int L;            // keys of the item's batch row (DECODE/CAUSAL; HYBRID: L per half)
-};
-
 
 // One workgroup = NW wavefronts; a wavefront owns QPW query slots, handled as
 // QPW/32 MFMA column blocks that share every K and V operand read from LDS
@@ -130,80 +83,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
   const int kg = KS ? w / NWQ : 0;
   const int wq = KS ? w - kg * NWQ : w;
 
-  // ---- work items.  The canonical order (index -> batch, kv head, query
-  // tile, key split) hands out the heaviest query tiles first.  With
-  // pairs_per_xcd > 0, index i runs on XCD i % 8 (workgroups are dealt to the
-  // 8 XCDs round-robin) and every query tile of a (batch, kv head) maps to
-  // one XCD, so its K/V stays in that XCD's L2.
-  const int P = a.B * a.Hkv;
-  // key ranges of an item: F is walked by the pipelined loop (every row of
-  // the item may see every key of it); R1 and R2 are the remaining keys the
-  // rows need, walked tile by tile with per-wavefront classification.
-  auto geom = [&](int idx, Geom& gm) {
-    if (a.pairs_per_xcd > 0) {
-      const int xcd = idx & 7, i = idx >> 3;
-      gm.pair = xcd * a.pairs_per_xcd + i % a.pairs_per_xcd;
-      gm.qt = a.n_qtiles - 1 - i / a.pairs_per_xcd;
-      gm.split = 0;
-    } else {
-      gm.split = idx % a.n_splits;
-      const int rest = idx / a.n_splits;
-      gm.pair = rest % P;
-      gm.qt = a.n_qtiles - 1 - rest / P;
-    }
-    Span F{0, 0}, R1{0, 0}, R2{0, 0};
-    if constexpr (VARLEN) gm.L = a.L;
-    if (a.mode == kHybrid) {
-      const int p0 = gm.qt * a.rows_per_wg;
-      const int p1 = imin(a.L, p0 + a.rows_per_wg);
-      const int e = imin(a.L, ((p1 - 1) / a.blk + 1) * a.blk);
-      const int s_min = (p0 / a.blk) * a.blk;   // clean prefix every row of the item sees
-      F = Span{a.L, a.L + (s_min / kBN) * kBN};
-      R1 = Span{F.hi, a.L + e};                 // rest of the clean prefix / own clean blocks
-      R2 = Span{s_min, e};                      // noisy blocks of these rows
-    } else {
-      int Lb = a.L;
-      if constexpr (VARLEN) {
-        Lb = imin(a.L, imax(a.n, a.kv_len[gm.pair / a.Hkv]));
-        gm.L = Lb;
-      }
-      const int r0 = gm.qt * a.rows_per_wg;
-      const int r1 = imin(a.n, r0 + a.rows_per_wg);
-      const int lo = gm.split * a.split_keys;
-      const int hi = imin(a.mode == kDecode ? Lb : Lb - a.n + r1, lo + a.split_keys);
-      const int full_hi = imin(hi, a.mode == kDecode ? Lb : Lb - a.n + r0 + 1);
-      const int nfull = full_hi > lo ? (full_hi - lo) / kBN : 0;
-      F = Span{lo, lo + nfull * kBN};
-      R1 = Span{F.hi, imax(F.hi, hi)};
-    }
-    // The persistent walk needs a boundary tile at the end of every item (its
-    // ring wait relies on it); an item of full tiles only gives up its last.
-    if (STAGES == 4 && R1.hi <= R1.lo && R2.hi <= R2.lo && F.hi > F.lo) {
-      F.hi -= kBN;
-      R1 = Span{F.hi, F.hi + kBN};
-    }
-    gm.F = F;
-    gm.R1 = R1;
-    gm.R2 = R2;
-    gm.nf = (F.hi - F.lo) / kBN;
-    gm.n1 = R1.hi > R1.lo ? (R1.hi - R1.lo + kBN - 1) / kBN : 0;
-    const int n2 = R2.hi > R2.lo ? (R2.hi - R2.lo + kBN - 1) / kBN : 0;
-    gm.nt = gm.nf + gm.n1 + n2;
-  };
-  // first and last key of tile j of an item (j clamped to the last tile)
-  auto tile_in = [&](const Geom& gm, int j, int& t0, int& t1) {
-    j = imin(j, gm.nt - 1);
-    if (j < gm.nf) {
-      t0 = gm.F.lo + j * kBN;
-      t1 = t0 + kBN;
-    } else if (j < gm.nf + gm.n1) {
-      t0 = gm.R1.lo + (j - gm.nf) * kBN;
-      t1 = imin(gm.R1.hi, t0 + kBN);
-    } else {
-      t0 = gm.R2.lo + (j - gm.nf - gm.n1) * kBN;
-      t1 = imin(gm.R2.hi, t0 + kBN);
-    }
-  };
+  // ---- work items and their key ranges (attn_index.h)
+  constexpr int WALK = STAGES == 4 ? kWalkPersistent : (STAGES == 5 ? kWalkSplit : kWalkRegs);
+  auto geom = [&](int idx, Geom& gm) { attn_geom(a, WALK, VARLEN ? a.kv_len : nullptr, idx, gm); };
+  auto tile_in = [&](const Geom& gm, int j, int& t0, int& t1) { attn_tile(gm, j, t0, t1); };
 
   // ---- the item being computed
   Geom cur{};
@@ -219,29 +102,19 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
     geom(idx, cur);
     b = cur.pair / a.Hkv;
     g = cur.pair - b * a.Hkv;
-    const size_t kvoff = (size_t)cur.pair * a.Sk * D;
+    const size_t kvoff = attn_kv_elem<D>(a, cur.pair, 0);
     kbase = a.k + kvoff;
     vbase = a.v + kvoff;
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
-      if (a.mode == kHybrid) {
+      if (a.mode == kHybrid) {   // waves [0, NW/2) hold the noisy rows, the rest the clean ones
         const int per_half = NW / 2;
         const int half = w / per_half;
-        const int s = ((w - half * per_half) * NQB + qb) * 32 + ql;
-        const int rloc = s / a.G;
-        const int pos = cur.qt * a.rows_per_wg + rloc;
-        valid[qb] = rloc < a.rows_per_wg && pos < a.L;
-        qrow[qb] = half * a.L + pos;
-        head[qb] = g * a.G + (s - rloc * a.G);
+        valid[qb] = attn_slot(a, half, ((w - half * per_half) * NQB + qb) * 32 + ql, cur.qt, g, qrow[qb], head[qb]);
       } else {
-        const int s = (wq * NQB + qb) * 32 + ql;
-        const int rloc = s / a.G;
-        const int r = cur.qt * a.rows_per_wg + rloc;
-        valid[qb] = rloc < a.rows_per_wg && r < a.n;
-        qrow[qb] = r;
-        head[qb] = g * a.G + (s - rloc * a.G);
+        valid[qb] = attn_slot(a, 0, (wq * NQB + qb) * 32 + ql, cur.qt, g, qrow[qb], head[qb]);
       }
-      const uint16_t* qp = a.q + ((size_t)(b * a.Hq + head[qb]) * a.Sq + qrow[qb]) * D + 8 * hb;
+      const uint16_t* qp = a.q + attn_q_elem<D>(a, b, head[qb], qrow[qb]) + 8 * hb;
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
         u32x4 x = valid[qb] ? *(const u32x4*)(qp + 16 * ks) : u32x4{0, 0, 0, 0};
@@ -557,7 +430,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
     }
   };
   auto dma_keys = [&](int pair, int t0, int t1, int stage) __attribute__((always_inline)) {
-    const size_t row0 = ((size_t)pair * a.Sk + t0) * D;
+    const size_t row0 = attn_kv_elem<D>(a, pair, t0);
     dma_at(a.k + row0, a.v + row0, t1 - t0, stage);
   };
   auto dma = [&](const Geom& gm, int j, int stage) __attribute__((always_inline)) {
@@ -638,8 +511,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       if (a.n_splits == 1) {
         const float inv = 1.f / l_tot;
         if (LSE && hb == 0)
-          a.lse[(size_t)(b * a.Hq + head[qb]) * a.Sq + qrow[qb]] = (m_run[qb] * sl2 + __log2f(l_tot)) * 0.6931471805599453f;
-        uint16_t* op = a.out + ((size_t)(b * a.Hq + head[qb]) * a.Sq + qrow[qb]) * D + 4 * hb;
+          a.lse[attn_q_row(a, b, head[qb], qrow[qb])] = (m_run[qb] * sl2 + __log2f(l_tot)) * 0.6931471805599453f;
+        uint16_t* op = a.out + attn_q_elem<D>(a, b, head[qb], qrow[qb]) + 4 * hb;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -651,9 +524,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
           }
         }
       } else {
-        const size_t rows = (size_t)a.B * a.Hq * a.n;
-        const size_t row = (size_t)(b * a.Hq + head[qb]) * a.n + qrow[qb];
-        float* po = a.part_o + ((size_t)cur.split * rows + row) * D + 4 * hb;
+        const size_t prow = attn_part_row(a, cur.split, b, head[qb], qrow[qb]);
+        float* po = a.part_o + attn_part_elem<D>(a, cur.split, b, head[qb], qrow[qb]) + 4 * hb;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -663,7 +535,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
           }
         }
         if (hb == 0) {
-          float* pm = a.part_ml + ((size_t)cur.split * rows + row) * 2;
+          float* pm = a.part_ml + prow * 2;
           pm[0] = m_run[qb] == -INFINITY ? -INFINITY : m_run[qb] * sl2;
           pm[1] = l_tot;
         }
@@ -798,15 +670,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
     // stream tile s, filled three tiles ahead, so the first tiles of the
     // next item load while the current one finishes.
     const int GR = gridDim.x, wg = blockIdx.x;
-    auto item_of = [&](int r) -> int {
-      if (a.pairs_per_xcd > 0) {
-        const int NL = GR >> 3, wl = wg >> 3;
-        const int i = r * NL + ((r & 1) ? NL - 1 - wl : wl);
-        return i < (a.n_items >> 3) ? i * 8 + (wg & 7) : -1;
-      }
-      const int i = r * GR + ((r & 1) ? GR - 1 - wg : wg);
-      return i < a.n_items ? i : -1;
-    };
+    auto item_of = [&](int r) -> int { return attn_item_of(a, GR, wg, r); };
     // Prefetch cursor: the next tile of the DMA stream, [c_t0, min(c_t0 + 64,
     // c_hi)) of key range c_reg (0: F, 1: R1, 2: R2) of item round c_r
     // (geometry cg), kept as a running key position so that a tile costs a
@@ -820,7 +684,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
     auto c_set = [&](const Span& sr) __attribute__((always_inline)) {
       c_t0 = sr.lo;
       c_hi = sr.hi;
-      c_kv = ((size_t)cg.pair * a.Sk + c_t0) * (2 * D);
+      c_kv = attn_kv_elem<D>(a, cg.pair, c_t0) * 2;
     };
     auto c_range = [&]() __attribute__((always_inline)) -> bool {
       if (c_reg == 0) {
@@ -1137,15 +1001,39 @@ static int device_cus() {
   return n;
 }
 
+long long attn_persistent_grid(const AttnPlan& p, int cus, int* pairs_per_xcd) {
+  // as many workgroups as fit at once (by LDS: one per compute unit at d =
+  // 128, two below) walk their shares of the items
+  const long long slots = (long long)cus * (p.d == 128 ? 1 : 2);
+  const long long grid = p.grid < slots ? p.grid : slots;
+  *pairs_per_xcd = (p.pairs_per_xcd > 0 && grid % 8 == 0) ? p.pairs_per_xcd : 0;
+  return grid;
+}
+
+void attn_fill_index(const AttnPlan& p, AttnIndex* a) {
+  a->B = p.B;
+  a->Hq = p.Hq;
+  a->Hkv = p.Hkv;
+  a->G = p.G;
+  a->mode = p.mode;
+  a->L = p.L;
+  a->n = p.n;
+  a->blk = p.blk;
+  a->Sq = p.Sq;
+  a->Sk = p.Sk;
+  a->rows_per_wg = p.rows_per_wg;
+  a->n_qtiles = p.n_qtiles;
+  a->n_splits = p.n_splits;
+  a->split_keys = p.split_keys;
+  a->pairs_per_xcd = p.pairs_per_xcd;
+  a->n_items = (int)p.grid;
+}
+
 template <int D>
 static hipError_t launch_d(const AttnPlan& p, AttnArgs a, hipStream_t st) {
   hipError_t e;
   if (p.stages == 4) {
-    // persistent: as many workgroups as fit at once (by LDS: one per compute
-    // unit at d = 128, two below) walk their shares of the items
-    const long long slots = (long long)device_cus() * (D == 128 ? 1 : 2);
-    long long grid = p.grid < slots ? p.grid : slots;
-    if (a.pairs_per_xcd > 0 && grid % 8 != 0) a.pairs_per_xcd = 0;
+    const long long grid = attn_persistent_grid(p, device_cus(), &a.pairs_per_xcd);
     e = launch_main<D, 8, 32, 4>(a, grid, st);
   } else if (p.stages == 5) {
     e = launch_main<D, 8, 32, 5>(a, p.grid, st);
@@ -1189,22 +1077,7 @@ hipError_t attn_launch(const AttnPlan& p, const void* q, const void* k, const vo
     a.part_o = (float*)ws;
     a.part_ml = (float*)((char*)ws + (size_t)p.n_splits * rows * p.d * 4);
   }
-  a.B = p.B;
-  a.Hq = p.Hq;
-  a.Hkv = p.Hkv;
-  a.G = p.G;
-  a.mode = p.mode;
-  a.L = p.L;
-  a.n = p.n;
-  a.blk = p.blk;
-  a.Sq = p.Sq;
-  a.Sk = p.Sk;
-  a.rows_per_wg = p.rows_per_wg;
-  a.n_qtiles = p.n_qtiles;
-  a.n_splits = p.n_splits;
-  a.split_keys = p.split_keys;
-  a.pairs_per_xcd = p.pairs_per_xcd;
-  a.n_items = (int)p.grid;
+  attn_fill_index(p, &a);
   a.sl2 = 1.4426950408889634f / sqrtf((float)p.d);
   (void)hipGetLastError();
   switch (p.d) {

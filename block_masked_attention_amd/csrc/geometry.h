@@ -18,6 +18,7 @@
 #pragma once
 
 #ifdef __HIPCC__
+#include <hip/hip_runtime.h>
 #define BDA_HD __host__ __device__ __forceinline__
 #else
 #define BDA_HD inline

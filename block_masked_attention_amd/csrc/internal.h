@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "attn_index.h"
+
 namespace bda {
 
 // Work decomposition of one attention call.  Both the workspace query and the
@@ -26,6 +28,11 @@ struct AttnPlan {
 
 int attn_make_plan(int B, int Hq, int Hkv, int L, int d, int block, int mode, AttnPlan* p,
                    const char** why);
+// The index arguments of the forward kernels for a plan, and the grid of the
+// persistent walk on a device of cus compute units (with the XCD-aware
+// order's pairs per XCD it can keep, 0 when it cannot).
+void attn_fill_index(const AttnPlan& p, AttnIndex* a);
+long long attn_persistent_grid(const AttnPlan& p, int cus, int* pairs_per_xcd);
 hipError_t attn_launch(const AttnPlan& p, const void* q, const void* k, const void* v, void* out,
                        float* lse, const int32_t* kv_len, void* ws, hipStream_t st);
 

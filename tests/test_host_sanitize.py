@@ -9,8 +9,11 @@
   linked with tests/host/abi_driver.cpp, which drives every path that runs
   before a launch: argument validation of every entry point, the plans
   behind the workspace-size queries, the tile classifier, the SPRINT keep
-  counts, and the host replay of the attention kernels' index arithmetic.
-  Nothing touches a device.
+  counts; and with tests/host/index_replay.cpp, which replays the attention
+  kernels' index arithmetic (attn_index.h) for the benchmark's workloads,
+  multi-item and ragged cases and workloads past 2^31 elements, checking
+  item coverage, tile bounds, key coverage and every global offset against
+  its tensor.  Nothing touches a device.
 """
 import os
 import shutil
@@ -51,7 +54,8 @@ def test_library_host_code_under_asan_ubsan(tmp_path):
              "-I", os.path.join(ROOT, "include"), "-I", CSRC]
     objs = []
     srcs = [os.path.join(CSRC, f) for f in ("attn.hip", "bwd.hip", "cache.hip", "commit.hip", "sprint.hip",
-                                             "api.cpp")] + [os.path.join(HOST, "abi_driver.cpp")]
+                                             "api.cpp")] + [os.path.join(HOST, "abi_driver.cpp"),
+                                                            os.path.join(HOST, "index_replay.cpp")]
     procs = []
     for s in srcs:
         o = str(tmp_path / (os.path.basename(s) + ".o"))
@@ -61,8 +65,10 @@ def test_library_host_code_under_asan_ubsan(tmp_path):
     for p in procs:
         _, err = p.communicate(timeout=900)
         assert p.returncode == 0, err[-4000:]
-    exe = str(tmp_path / "abi_driver")
-    subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-Xarch_host", "-fsanitize=address", "-Xarch_host",
-                           "-fsanitize=undefined", *objs, "-o", exe])
-    # the HIP runtime itself is not instrumented: leak reports would be its own
-    _run(exe, dict(SAN_ENV, ASAN_OPTIONS="detect_leaks=0"))
+    lib_objs, drivers = objs[:-2], objs[-2:]
+    for drv in drivers:
+        exe = drv[:-2]
+        subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-Xarch_host", "-fsanitize=address", "-Xarch_host",
+                               "-fsanitize=undefined", *lib_objs, drv, "-o", exe])
+        # the HIP runtime itself is not instrumented: leak reports would be its own
+        _run(exe, dict(SAN_ENV, ASAN_OPTIONS="detect_leaks=0"))
