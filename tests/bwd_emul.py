@@ -5,7 +5,10 @@ enters the row deltas D = rowsum(dO * O)), P and dS are rounded to bf16 as
 MFMA operands, and the gradients are stored in bf16.  This torch CPU
 computation rounds at exactly those points and computes everything else in
 fp32; its distance to the exact fp64 gradients is the rounding error that
-choice of precision implies, against which the GPU error is judged.
+choice of precision implies, against which the GPU error is judged.  It
+takes the same bf16 forward output O that the GPU backward is given (an
+input of the backward), so that the two differ only by the backward's own
+rounding.
 """
 import math
 
@@ -18,9 +21,11 @@ def _bf(x):
     return x.to(torch.bfloat16).to(torch.float32)
 
 
-def grads(q, k, v, do, L, block):
+def grads(q, k, v, do, L, block, o=None):
     """dq, dk, dv (float64 tensors) of the hybrid-mask attention with the
-    rounding points described above.  q, do: [B,Hq,2L,d]; k, v: [B,Hkv,2L,d]."""
+    rounding points described above.  q, do: [B,Hq,2L,d]; k, v: [B,Hkv,2L,d].
+    o (optional, [B,Hq,2L,d] bf16): the forward output the backward is given;
+    when absent it is the bf16 rounding of the fp32 attention output."""
     M = torch.from_numpy(oracle.mask("hybrid", L, block).astype(bool))
     B, Hq, S, d = q.shape
     Hkv = k.shape[1]
@@ -37,8 +42,8 @@ def grads(q, k, v, do, L, block):
             s = s.masked_fill(~M, float("-inf"))
             lse = torch.logsumexp(s.double(), dim=-1).float()
             p = torch.exp(s - lse[:, None])
-            o = _bf(p @ vf[b, g])
-            D = (gf[b, h] * o).sum(-1)
+            ob = _bf(p @ vf[b, g]) if o is None else o[b, h].to(torch.float32)
+            D = (gf[b, h] * ob).sum(-1)
             dp = gf[b, h] @ vf[b, g].T
             ds = _bf(p * (dp - D[:, None]))
             dq[b, h] = _bf(scale * (ds @ kf[b, g]))

@@ -8,7 +8,8 @@ the same bf16 inputs.  Tolerance (derived from the arithmetic; see
 bwd_emul.py): a CPU computation that rounds at the GPU path's bf16 points
 gives the error that precision implies; the GPU's largest and mean absolute
 errors against the oracle must stay within twice that computation's own
-(plus 1e-3 of the gradient's rms for the max).
+(plus 1e-3 of the gradient's rms for the max), and so must every element's
+(plus 2^-6 of the element's magnitude and of the gradient's rms).
 """
 import numpy as np
 import pytest
@@ -23,16 +24,31 @@ pytestmark = pytest.mark.gpu
 bda = pytest.importorskip("block_masked_attention_amd")
 
 
+# Per element: |gpu - ref| <= 2 |emul - ref| + EPS_REL (|ref| + rms).  The
+# GPU and the emulation take the same bf16 forward output and round at the
+# same points, but from fp32 values summed in different orders, so a bf16
+# rounding of P, dS or the stored gradient can land one step apart (2^-8
+# relative); EPS_REL = 2^-6 covers such a step in the stored value and a few
+# in the terms summed into it, and the rms term does the same for elements
+# whose exact value is near zero.
+EPS_REL = 2.0 ** -6
+
+
 def _check(got, ref, emul, what):
     got = got.float().cpu().numpy().astype(np.float64)
     emul = emul.numpy()
     rms = float(np.sqrt(np.mean(ref * ref))) + 1e-30
     err, eref = np.abs(got - ref), np.abs(emul - ref)
+    bound = 2 * eref + EPS_REL * (np.abs(ref) + rms)
+    worst = float((err / bound).max())
     say(f"[bwd] {what}: max err {err.max() / rms:.3e} rms (bf16-rounding yardstick {eref.max() / rms:.3e}), "
-        f"mean err {err.mean() / rms:.3e} rms (yardstick {eref.mean() / rms:.3e})")
+        f"mean err {err.mean() / rms:.3e} rms (yardstick {eref.mean() / rms:.3e}), "
+        f"largest err / per-element bound {worst:.3f}")
     assert np.isfinite(got).all(), f"{what}: non-finite"
     assert err.max() <= 2 * eref.max() + 1e-3 * rms, f"{what}: largest error beyond the bound"
     assert err.mean() <= 2 * eref.mean() + 1e-6 * rms, f"{what}: mean error beyond the bound"
+    bad = err > bound
+    assert not bad.any(), f"{what}: {int(bad.sum())} of {bad.size} elements beyond the per-element bound"
 
 
 CASES = [
@@ -57,7 +73,7 @@ def test_bwd_elementwise(B, Hq, Hkv, L, d, blk):
     dq, dk, dv = bda.attn_bwd(qd, kd, vd, out, dod, lse, blk)
     torch.cuda.synchronize()
     rq, rk, rv, rl = oracle.attention_bwd("hybrid", q, k, v, do, L, blk)
-    eq, ek, ev = bwd_emul.grads(q, k, v, do, L, blk)
+    eq, ek, ev = bwd_emul.grads(q, k, v, do, L, blk, o=out.cpu())
     assert np.allclose(lse.cpu().numpy(), rl, rtol=0, atol=2e-3), "forward log-sum-exp"
     what = f"B={B} Hq={Hq} Hkv={Hkv} L={L} d={d} b={blk}"
     _check(dq, rq, eq, what + " dq")
@@ -91,7 +107,7 @@ def test_bwd_training_form_full_size_batch0():
     dq, dk, dv = bda.attn_bwd(qd, kd, vd, out, dod, lse, case.block)
     torch.cuda.synchronize()
     rq, rk, rv, _ = oracle.attention_bwd("hybrid", case.q[:1], case.k[:1], case.v[:1], do[:1], case.L, case.block)
-    eq, ek, ev = bwd_emul.grads(case.q[:1], case.k[:1], case.v[:1], do[:1], case.L, case.block)
+    eq, ek, ev = bwd_emul.grads(case.q[:1], case.k[:1], case.v[:1], do[:1], case.L, case.block, o=out[:1].cpu())
     _check(dq[:1], rq, eq, "training form batch 0 dq")
     _check(dk[:1], rk, ek, "training form batch 0 dk")
     _check(dv[:1], rv, ev, "training form batch 0 dv")
