@@ -434,6 +434,14 @@ def secondary(bda, synth, torch, dev, args):
     del k, v, qs, lg, out, ws, cws
     torch.cuda.empty_cache()
 
+    # ---- the canvas denoise step captured as one HIP graph: append the
+    # active block's fresh K/V rows, DECODE attention over the cache (per-row
+    # lengths on the device), row statistics, adaptive stopping and the
+    # commit; and the number of steps the whole 256-position canvas takes
+    res["canvas_graph"] = canvas_graph(bda, synth, torch, dev, iters)
+    log(f"[bench] canvas_graph: {res['canvas_graph']}")
+    torch.cuda.empty_cache()
+
     # ---- commit on decode-form logits [32, 28, 131072] bf16, threshold 0.85
     logits, idx, masked0 = synth.commit_logits()
     G, R, V = logits.shape
@@ -547,6 +555,125 @@ def secondary(bda, synth, torch, dev, args):
                      "algorithmic_bytes": byts}
     log(f"[bench] verify: {res['verify']}")
     return res
+
+
+def canvas_graph(bda, synth, torch, dev, iters):
+    """One denoise step of the multimodal canvas (B=2, 28-row active block,
+    threshold 0.9, at least one commit) as eager launches and as one HIP
+    graph replay, beside the HBM floors of its attention and commit; then
+    the whole canvas run block by block with the graph (the host reads the
+    commit mask after each step to move to the next block), reporting the
+    steps it took against the 48-step budget."""
+    B, Hq, Hkv, d, V = 2, 32, 8, 128, synth.VOCAB
+    n = synth.CANVAS_BLOCK
+    cap = synth.PREFIX + synth.CANVAS
+    pre = synth.multimodal_prefill()
+    kc = torch.zeros(B, Hkv, cap, d, dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    kc[:, :, :synth.PREFIX] = pre.k.to(dev)
+    vc[:, :, :synth.PREFIX] = pre.v.to(dev)
+    del pre
+    u8, i32, i64, f32 = torch.uint8, torch.int32, torch.int64, torch.float32
+    kl = torch.full((B,), synth.PREFIX + n, dtype=i32, device=dev)
+    st = {}
+
+    def buffers(nb):
+        if nb in st:
+            return st[nb]
+        x = dict(q=torch.empty(B, Hq, nb, d, dtype=torch.bfloat16, device=dev),
+                 kb=torch.empty(B, Hkv, nb, d, dtype=torch.bfloat16, device=dev),
+                 logits=torch.empty(B, nb, V, dtype=torch.bfloat16, device=dev),
+                 tokens=torch.full((B, nb), -1, dtype=i64, device=dev),
+                 masked=torch.ones(B, nb, dtype=u8, device=dev),
+                 conf=torch.empty(B, nb, dtype=f32, device=dev), am=torch.empty(B, nb, dtype=i64, device=dev),
+                 ent=torch.empty(B, nb, dtype=f32, device=dev), mean=torch.empty(B, dtype=f32, device=dev),
+                 prev=torch.full((B, nb), -1, dtype=i64, device=dev), stable=torch.zeros(B, dtype=i32, device=dev),
+                 frozen=torch.zeros(B, dtype=u8, device=dev), nfz=torch.zeros(1, dtype=i32, device=dev))
+        x["vb"] = torch.empty_like(x["kb"])
+        x["out"] = torch.empty_like(x["q"])
+        x["ws_a"] = torch.empty(max(1, bda.attn_workspace_bytes(B, Hq, Hkv, cap, d, nb, "decode")), dtype=u8,
+                                device=dev)
+        x["ws_c"] = torch.empty(bda.lib.bda_commit_workspace_bytes(B, nb, V), dtype=u8, device=dev)
+        x["ws_s"] = torch.empty(bda.lib.bda_row_stats_workspace_bytes(B, nb, V), dtype=u8, device=dev)
+        st[nb] = x
+        return x
+
+    def attention(x, nb):
+        bda.attn_fwd_varlen(x["q"], kc, vc, kl, "decode", nb, out=x["out"], workspace=x["ws_a"])
+
+    def step(x, nb):
+        bda.kv_append(kc, vc, x["kb"], x["vb"], kl)
+        attention(x, nb)
+        bda.row_stats(x["logits"], workspace=x["ws_s"], out=(x["conf"], x["am"], x["ent"], x["mean"]))
+        bda.adaptive_stop(x["am"], x["prev"], x["stable"], x["frozen"], x["mean"], 1, 0.005, n_frozen=x["nfz"])
+        bda.commit(x["logits"], x["tokens"], x["masked"], 0.9, 1, workspace=x["ws_c"])
+
+    def load(x, s_, nb):
+        q, kb, vb, lg, _ = synth.multimodal_step(s_, nb, B=B)
+        x["q"].copy_(q)
+        x["kb"].copy_(kb)
+        x["vb"].copy_(vb)
+        x["logits"].copy_(lg)
+
+    x = buffers(n)
+    load(x, 0, n)
+    graphs = {}
+
+    def graph_of(nb, fn):
+        key = (nb, fn.__name__)
+        if key not in graphs:
+            xb = buffers(nb)
+            for _ in range(2):
+                fn(xb, nb)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn(xb, nb)
+            torch.cuda.synchronize()
+            graphs[key] = g
+        return graphs[key]
+
+    def reset(i):
+        x["masked"].fill_(1)
+
+    t_eager, _ = time_launches(lambda i: step(x, n), iters, 5, pre=reset)
+    g_step = graph_of(n, step)
+    t_graph, _ = time_launches(lambda i: g_step.replay(), iters, 5, pre=reset)
+    t_graph_host, _ = time_launches(lambda i: g_step.replay(), iters, 5, pre=reset, queue=False)
+    g_att = graph_of(n, attention)
+    t_att_graph, _ = time_launches(lambda i: g_att.replay(), iters, 5)
+    t_att_eager, _ = time_launches(lambda i: attention(x, n), iters, 5)
+    L0 = synth.PREFIX + n
+    att_bytes = B * Hq * n * d * 2 * 2 + B * Hkv * L0 * d * 2 * 2
+    com_bytes = B * n * V * 2
+    floor = (att_bytes + 2 * com_bytes + B * Hkv * n * d * 2 * 2) / PEAK_HBM_GBS / 1e3
+
+    # the whole canvas: blocks of 28 (a last one of 4) in lockstep over the batch
+    kl.fill_(synth.PREFIX)
+    steps, pos, committed = 0, 0, 0
+    for nb in synth.canvas_blocks():
+        xb = buffers(nb)
+        xb["masked"].fill_(1)
+        xb["tokens"].fill_(-1)
+        kl.add_(nb)                                  # the block's rows join the cache
+        g = graph_of(nb, step)
+        while True:
+            load(xb, steps, nb)
+            g.replay()
+            steps += 1
+            left = int(xb["masked"].sum().item())
+            if left == 0 or steps >= 400:
+                break
+        committed += B * nb - left
+        pos += nb
+    torch.cuda.synchronize()
+    return {"B": B, "n": n, "kv_len_first_block": L0, "V": V,
+            "us_per_step_eager": round(t_eager * 1e3, 2), "us_per_step_graph": round(t_graph * 1e3, 2),
+            "us_per_step_graph_as_issued": round(t_graph_host * 1e3, 2),
+            "attention_us_graph": round(t_att_graph * 1e3, 2), "attention_us_eager": round(t_att_eager * 1e3, 2),
+            "attention_floor_us": round(att_bytes / PEAK_HBM_GBS / 1e3, 2),
+            "step_hbm_floor_us": round(floor, 2),
+            "canvas_positions": pos, "canvas_steps": steps, "step_budget": 48, "committed_tokens": committed}
 
 
 def speculative_step(bda, synth, torch, dev, iters):
