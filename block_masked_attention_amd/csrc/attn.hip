@@ -701,11 +701,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       }
       return false;
     };
+    // Past the last item the cursor rests on a stand-in tile: key 0 of the
+    // first (batch, kv head), one key, re-issued by every later step.
     auto c_next_item = [&]() __attribute__((always_inline)) {
       for (;;) {
         const int idx = item_of(++c_r);
         if (idx < 0) {
           c_live = false;
+          c_t0 = 0;
+          c_hi = 1;
+          c_kv = 0;
+          --c_r;
           return;
         }
         geom(idx, cg);
@@ -714,14 +720,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       }
     };
     c_next_item();
-    // Returns whether a tile was issued.  The wait at the end of a tile step
-    // leaves only the newest tile in flight, so the tile the next step reads
-    // must not be the newest: every item ends with a boundary tile (see the
-    // geometry), fast steps are always followed by at least one more issued
-    // tile, and a boundary step that finds the stream exhausted waits for
-    // every load before it reads its tile.
+    // Issues one load per call and returns whether it was a tile of the
+    // stream.  The wait at the end of a tile step leaves only the newest
+    // issue in flight, and a fast step i reads tiles i and i + 1, so an issue
+    // must follow tile i + 1: once the stream is exhausted every call issues
+    // the stand-in into the stage the previous step freed, which no step
+    // reads.  Every item ends with a boundary tile (see the geometry), and a
+    // boundary step whose issue was the stand-in waits for every load before
+    // it reads its tile.
     auto c_issue = [&](int st) __attribute__((always_inline)) -> bool {
-      if (!c_live) return false;
+      const bool live = c_live;
       const int t1 = imin(c_hi, c_t0 + kBN);
       dma_at(a.k + c_kv / 2, a.v + c_kv / 2, t1 - c_t0, st);
       c_t0 += kBN;
@@ -730,7 +738,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
         ++c_reg;
         if (!c_range()) c_next_item();
       }
-      return true;
+      return live;
     };
     int sp = 0;   // stream position of the current item's first tile
     auto stg = [&](int i) { return (sp + i) & 3; };

@@ -10,12 +10,19 @@
 //    valid row sees, and the key splits of a query tile partition the keys;
 //  * every global element offset the kernels form (Q and O rows, K and V rows
 //    of each DMA lane, log-sum-exp entries, split partials) stays inside its
-//    tensor, in 64-bit arithmetic, including workloads past 2^31 elements.
-// Prints "ok" and returns 0 when every check held.
+//    tensor, in 64-bit arithmetic, including workloads past 2^31 elements;
+//  * the persistent walk's DMA ring: replaying each workgroup's sequence of
+//    issues, waits and reads, every tile a step reads has landed and still
+//    owns its stage.
+// Prints "ok" and returns 0 when every check held.  With the argument
+// "no-stand-in" it replays the ring without the stand-in loads the walk
+// issues once its stream is exhausted, and must then report failures.
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <algorithm>
+#include <string>
 #include <vector>
 
 #include "attn_index.h"
@@ -65,6 +72,71 @@ static void dma_lanes(const AttnIndex& a, int pair, int t0, int t1, size_t kv_ro
     }
 }
 
+static bool g_stand_in = true;
+
+// The persistent walk's DMA ring as attn.hip runs it.  Stream tile t of a
+// workgroup (its items' tiles in order) goes to stage t % 4, issued three
+// steps ahead; the prologue issues three and waits for all.  An item starts
+// by waiting for every load (its Q operands).  Every step first issues one
+// load: the next stream tile or, once the stream is exhausted, the stand-in,
+// into the stage the previous step freed.  Fast step i of an item reads
+// stream tiles i and i + 1 (the next tile's K); a boundary step reads tile
+// i, after waiting for every load when its issue was the stand-in.  Every
+// step ends by waiting for all loads but the newest, then the barrier.
+static void ring_replay(const AttnIndex& a, const int32_t* kv_len, long long grid, const char* what) {
+  for (long long wg = 0; wg < grid; ++wg) {
+    std::vector<Geom> items;
+    long long T = 0;
+    for (int r = 0;; ++r) {
+      const int idx = attn_item_of(a, (int)grid, (int)wg, r);
+      if (idx < 0) break;
+      Geom gm;
+      attn_geom(a, kWalkPersistent, kv_len, idx, gm);
+      items.push_back(gm);
+      T += gm.nt;
+    }
+    std::vector<long long> issue_of((size_t)T, -1);
+    long long owner[4] = {-1, -1, -1, -1};   // issue that last wrote each stage
+    long long issued = 0, landed = 0, next_tile = 0;
+    // issue at stream position pos; returns whether it was a stream tile
+    auto issue = [&](long long pos) -> bool {
+      if (next_tile < T) {
+        CHECK(next_tile == pos, "%s: wg %lld issues tile %lld at position %lld", what, wg, next_tile, pos);
+        issue_of[(size_t)next_tile++] = issued;
+        owner[pos & 3] = issued++;
+        return true;
+      }
+      if (g_stand_in) owner[pos & 3] = issued++;
+      return false;
+    };
+    auto read = [&](long long t) {
+      const bool ok = t < T && issue_of[(size_t)t] >= 0 && issue_of[(size_t)t] < landed &&
+                      owner[t & 3] == issue_of[(size_t)t];
+      CHECK(ok, "%s: wg %lld reads stream tile %lld of %lld before it landed or after its stage was reused", what,
+            wg, t, T);
+    };
+    auto settle = [&]() { landed = std::max(landed, issued - 1); };
+    for (int k = 0; k < 3; ++k) issue(k);
+    landed = issued;
+    long long sp = 0;
+    for (const Geom& gm : items) {
+      landed = issued;
+      for (int i = 0; i < gm.nf; ++i) {
+        issue(sp + i + 3);
+        read(sp + i);
+        read(sp + i + 1);
+        settle();
+      }
+      for (int i = gm.nf; i < gm.nt; ++i) {
+        if (!issue(sp + i + 3)) landed = issued;
+        read(sp + i);
+        settle();
+      }
+      sp += gm.nt;
+    }
+  }
+}
+
 template <int D>
 static void replay(const char* what, int B, int Hq, int Hkv, int L, int block, int mode, const int32_t* kv_len,
                    int cus = 256) {
@@ -93,6 +165,7 @@ static void replay(const char* what, int B, int Hq, int Hkv, int L, int block, i
         if (idx < a.n_items) ++seen[(size_t)idx];
       }
     for (int i = 0; i < a.n_items; ++i) CHECK(seen[(size_t)i] == 1, "%s: item %d taken %d times", what, i, seen[(size_t)i]);
+    ring_replay(a, kv_len, grid, what);
   }
   for (int idx = 0; idx < a.n_items; ++idx) {
     Geom gm;
@@ -174,7 +247,8 @@ static void replay(const char* what, int B, int Hq, int Hkv, int L, int block, i
   }
 }
 
-int main() {
+int main(int argc, char** argv) {
+  if (argc > 1 && std::string(argv[1]) == "no-stand-in") g_stand_in = false;
   // the benchmark's workloads
   replay<128>("training form B4 L2048 b32", 4, 32, 8, 2048, 32, kHybrid, nullptr);
   replay<128>("prefill B2 n=L=4096", 2, 32, 8, 4096, 4096, kCausal, nullptr);

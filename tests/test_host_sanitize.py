@@ -12,8 +12,10 @@
   counts; and with tests/host/index_replay.cpp, which replays the attention
   kernels' index arithmetic (attn_index.h) for the benchmark's workloads,
   multi-item and ragged cases and workloads past 2^31 elements, checking
-  item coverage, tile bounds, key coverage and every global offset against
-  its tensor.  Nothing touches a device.
+  item coverage, tile bounds, key coverage, every global offset against
+  its tensor and the persistent walk's DMA ring protocol (run once more
+  without the walk's stand-in loads, where it must fail).  Nothing touches
+  a device.
 """
 import os
 import shutil
@@ -72,3 +74,10 @@ def test_library_host_code_under_asan_ubsan(tmp_path):
                                "-fsanitize=undefined", *lib_objs, drv, "-o", exe])
         # the HIP runtime itself is not instrumented: leak reports would be its own
         _run(exe, dict(SAN_ENV, ASAN_OPTIONS="detect_leaks=0"))
+    # the ring replay must catch a walk that stops issuing once its stream is
+    # exhausted: the last fast step of a workgroup's last item, when that
+    # item has one boundary tile (the causal prefill), would read a tile
+    # whose loads may still be in flight
+    p = subprocess.run([drivers[1][:-2], "no-stand-in"], capture_output=True, text=True, timeout=600,
+                       env=dict(SAN_ENV, ASAN_OPTIONS="detect_leaks=0"))
+    assert p.returncode != 0 and "before it landed" in p.stderr, (p.stdout + p.stderr)[-4000:]
