@@ -11,9 +11,9 @@
 //  * every global element offset the kernels form (Q and O rows, K and V rows
 //    of each DMA lane, log-sum-exp entries, split partials) stays inside its
 //    tensor, in 64-bit arithmetic, including workloads past 2^31 elements;
-//  * the persistent walk's DMA ring: replaying each workgroup's sequence of
-//    issues, waits and reads, every tile a step reads has landed and still
-//    owns its stage.
+//  * the DMA rings of the persistent and split-key walks: replaying each
+//    workgroup's sequence of issues, waits and reads, every tile a step
+//    reads has landed and still owns its stage.
 // Prints "ok" and returns 0 when every check held.  With the argument
 // "no-stand-in" it replays the ring without the stand-in loads the walk
 // issues once its stream is exhausted, and must then report failures.
@@ -137,6 +137,36 @@ static void ring_replay(const AttnIndex& a, const int32_t* kv_len, long long gri
   }
 }
 
+// The split-key walk's DMA ring as attn.hip runs it, for one item: tile t
+// goes to stage t % 5; the prologue issues up to four and waits for all.
+// Step i first issues the next tile (into the stage of tile i - 1, which the
+// step before finished), reads tile i, then waits until tile i + 1 has
+// landed (up to three tiles issued after it stay in flight) and the
+// barrier.
+static void split_ring_replay(const Geom& gm, const char* what, int idx) {
+  const int nt = gm.nt;
+  long long owner[5] = {-1, -1, -1, -1, -1};
+  long long issued = 0, landed = 0;
+  auto issue = [&]() {
+    if (issued >= nt) return;
+    owner[issued % 5] = issued;
+    ++issued;
+  };
+  auto read = [&](long long t) {
+    const bool ok = t < nt && t < landed && owner[t % 5] == t;
+    CHECK(ok, "%s: split item %d reads tile %lld of %d before it landed or after its stage was reused", what, idx,
+          t, nt);
+  };
+  for (int k = 0; k < 4; ++k) issue();
+  landed = issued;
+  for (int i = 0; i < nt; ++i) {
+    issue();
+    read(i);
+    const long long newer = std::min(3LL, std::max(0LL, issued - 1 - (i + 1)));
+    landed = std::max(landed, issued - newer);
+  }
+}
+
 template <int D>
 static void replay(const char* what, int B, int Hq, int Hkv, int L, int block, int mode, const int32_t* kv_len,
                    int cus = 256) {
@@ -209,6 +239,7 @@ static void replay(const char* what, int B, int Hq, int Hkv, int L, int block, i
       return -1;
     };
     CHECK(walk != kWalkPersistent || gm.nt == 0 || gm.nt > gm.nf, "%s: item %d ends with a full tile", what, idx);
+    if (walk == kWalkSplit) split_ring_replay(gm, what, idx);
     // query slots: bounds, key coverage, full tiles visible to every valid row
     const int halves = mode == kHybrid ? 2 : 1;
     const int slots = mode == kHybrid ? (nw / 2) * 32 : (walk == kWalkSplit ? nw / 2 : nw) * 32;
