@@ -720,18 +720,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       }
     };
     c_next_item();
-    // Issues one load per call and returns whether it was a tile of the
-    // stream.  The wait at the end of a tile step leaves only the newest
-    // issue in flight, and a fast step i reads tiles i and i + 1, so an issue
-    // must follow tile i + 1: once the stream is exhausted every call issues
-    // the stand-in into the stage the previous step freed, which no step
-    // reads.  Every item ends with a boundary tile (see the geometry), and a
-    // boundary step whose issue was the stand-in waits for every load before
-    // it reads its tile.
-    auto c_issue = [&](int st) __attribute__((always_inline)) -> bool {
+    // Issues the next tile of the stream and returns whether there was one.
+    // The wait at the end of a tile step leaves only the newest issue in
+    // flight, and a fast step i reads tiles i and i + 1, so an issue must
+    // follow tile i + 1: once the stream is exhausted a fast step issues the
+    // stand-in into the stage the previous step freed, which no step reads.
+    // Every item ends with a boundary tile (see the geometry), and a
+    // boundary step that finds the stream exhausted issues nothing and
+    // waits for every load before it reads its tile.
+    auto c_issue = [&](int st, bool stand_in) __attribute__((always_inline)) -> bool {
       const bool live = c_live;
       const int t1 = imin(c_hi, c_t0 + kBN);
-      dma_at(a.k + c_kv / 2, a.v + c_kv / 2, t1 - c_t0, st);
+      if (stand_in || live) dma_at(a.k + c_kv / 2, a.v + c_kv / 2, t1 - c_t0, st);
       c_t0 += kBN;
       c_kv += (size_t)kBN * 2 * D;
       if (__builtin_expect(c_t0 >= c_hi, 0)) {
@@ -742,9 +742,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
     };
     int sp = 0;   // stream position of the current item's first tile
     auto stg = [&](int i) { return (sp + i) & 3; };
-    c_issue(stg(0));
-    c_issue(stg(1));
-    c_issue(stg(2));
+    c_issue(stg(0), false);
+    c_issue(stg(1), false);
+    c_issue(stg(2), false);
     drain();
 #pragma unroll 1
     for (int r = 0;; ++r) {
@@ -831,14 +831,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
 #pragma unroll 1
         for (int i = 0; i < nf; ++i) {
           const int cu = stg(i);
-          c_issue(stg(i + 3));
+          c_issue(stg(i + 3), true);
           half_step(cu, 1, cu, 0, sb, sa);
           half_step(stg(i + 1), 0, cu, 1, sa, sb);
           settle();
         }
 #pragma unroll 1
         for (int i = nf; i < nt; ++i) {
-          if (!c_issue(stg(i + 3))) drain();
+          if (!c_issue(stg(i + 3), false)) drain();
           slow_tile(stg(i), i);
           settle();
         }

@@ -77,12 +77,13 @@ static bool g_stand_in = true;
 // The persistent walk's DMA ring as attn.hip runs it.  Stream tile t of a
 // workgroup (its items' tiles in order) goes to stage t % 4, issued three
 // steps ahead; the prologue issues three and waits for all.  An item starts
-// by waiting for every load (its Q operands).  Every step first issues one
-// load: the next stream tile or, once the stream is exhausted, the stand-in,
-// into the stage the previous step freed.  Fast step i of an item reads
-// stream tiles i and i + 1 (the next tile's K); a boundary step reads tile
-// i, after waiting for every load when its issue was the stand-in.  Every
-// step ends by waiting for all loads but the newest, then the barrier.
+// by waiting for every load (its Q operands).  Every step first issues the
+// next stream tile into the stage the previous step freed; once the stream
+// is exhausted a fast step issues the stand-in there instead and a
+// boundary step nothing.  Fast step i of an item reads stream tiles i and
+// i + 1 (the next tile's K); a boundary step reads tile i, after waiting
+// for every load when it had nothing to issue.  Every step ends by waiting
+// for all loads but the newest, then the barrier.
 static void ring_replay(const AttnIndex& a, const int32_t* kv_len, long long grid, const char* what) {
   for (long long wg = 0; wg < grid; ++wg) {
     std::vector<Geom> items;
@@ -99,14 +100,14 @@ static void ring_replay(const AttnIndex& a, const int32_t* kv_len, long long gri
     long long owner[4] = {-1, -1, -1, -1};   // issue that last wrote each stage
     long long issued = 0, landed = 0, next_tile = 0;
     // issue at stream position pos; returns whether it was a stream tile
-    auto issue = [&](long long pos) -> bool {
+    auto issue = [&](long long pos, bool stand_in) -> bool {
       if (next_tile < T) {
         CHECK(next_tile == pos, "%s: wg %lld issues tile %lld at position %lld", what, wg, next_tile, pos);
         issue_of[(size_t)next_tile++] = issued;
         owner[pos & 3] = issued++;
         return true;
       }
-      if (g_stand_in) owner[pos & 3] = issued++;
+      if (stand_in && g_stand_in) owner[pos & 3] = issued++;
       return false;
     };
     auto read = [&](long long t) {
@@ -116,19 +117,19 @@ static void ring_replay(const AttnIndex& a, const int32_t* kv_len, long long gri
             wg, t, T);
     };
     auto settle = [&]() { landed = std::max(landed, issued - 1); };
-    for (int k = 0; k < 3; ++k) issue(k);
+    for (int k = 0; k < 3; ++k) issue(k, false);
     landed = issued;
     long long sp = 0;
     for (const Geom& gm : items) {
       landed = issued;
       for (int i = 0; i < gm.nf; ++i) {
-        issue(sp + i + 3);
+        issue(sp + i + 3, true);
         read(sp + i);
         read(sp + i + 1);
         settle();
       }
       for (int i = gm.nf; i < gm.nt; ++i) {
-        if (!issue(sp + i + 3)) landed = issued;
+        if (!issue(sp + i + 3, false)) landed = issued;
         read(sp + i);
         settle();
       }
