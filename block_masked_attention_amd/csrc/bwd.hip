@@ -22,6 +22,8 @@
 // get P = 0.  fp32 accumulation, bf16 MFMA operands, bf16 gradients.
 #include <limits.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "geometry.h"
 #include "internal.h"
@@ -499,7 +501,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
   auto block = [&](int st) {
     const uint16_t* qb = qd + st * 2 * QE;
     const uint16_t* db = qb + QE;
-    const bool all_seen = seen_all(st);
+    const bool all_seen = __builtin_amdgcn_readfirstlane((int)seen_all(st)) != 0;   // uniform
     f32x16 sv{}, dp{};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -514,39 +516,53 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
     // slots' lse, delta and threshold are read as 4-vectors, half a block at
     // a time, so the reads are unconditional and masked pairs take
     // exp2(-inf) = 0 by a select (per-element reads were sunk into a branch
-    // and a full LDS wait per element).
+    // and a full LDS wait per element).  A block every slot of the wavefront
+    // sees whole takes one uniform branch to the same arithmetic without the
+    // per-pair tests and selects.
     bf16x8 pb[2], sb[2];
+    auto p_ds = [&](auto full_c) __attribute__((always_inline)) {
+      constexpr bool FULL = decltype(full_c)::value;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      f32x4 lv[2], dvv[2];
-      i32x4 tv[2];
+      for (int kk = 0; kk < 2; ++kk) {
+        f32x4 lv[2], dvv[2];
+        i32x4 tv[2];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int o = 8 * (2 * kk + u) + 4 * hb;
-        lv[u] = *(const f32x4*)(&sl[st][0][o]) * kLn2Inv;
-        dvv[u] = *(const f32x4*)(&sl[st][1][o]);
-        tv[u] = *(const i32x4*)(&sthr[st][o]);
-      }
-      u32x4 pk, dk4;
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        float pv[2], dv2[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int i = 8 * kk + 2 * e2 + h;
-          const int u = (2 * e2 + h) >> 2, x = i & 3;
-          const int t = tv[u][x];
-          const bool ok = all_seen | (clean & (kblk <= t)) | (!clean & (kblk == t));
-          const float p = exp2_fast(ok ? fmaf(sv[i], a.sl2, -lv[u][x]) : -INFINITY);
-          pv[h] = p;
-          dv2[h] = p * (dp[i] - dvv[u][x]);
+        for (int u = 0; u < 2; ++u) {
+          const int o = 8 * (2 * kk + u) + 4 * hb;
+          lv[u] = *(const f32x4*)(&sl[st][0][o]) * kLn2Inv;
+          dvv[u] = *(const f32x4*)(&sl[st][1][o]);
+          if (!FULL) tv[u] = *(const i32x4*)(&sthr[st][o]);
         }
-        pk[e2] = pack_bf16x2(pv[0], pv[1]);
-        dk4[e2] = pack_bf16x2(dv2[0], dv2[1]);
+        u32x4 pk, dk4;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          float pv[2], dv2[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int i = 8 * kk + 2 * e2 + h;
+            const int u = (2 * e2 + h) >> 2, x = i & 3;
+            float p;
+            if constexpr (FULL) {
+              p = exp2_fast(fmaf(sv[i], a.sl2, -lv[u][x]));
+            } else {
+              const int t = tv[u][x];
+              const bool ok = (clean & (kblk <= t)) | (!clean & (kblk == t));
+              p = exp2_fast(ok ? fmaf(sv[i], a.sl2, -lv[u][x]) : -INFINITY);
+            }
+            pv[h] = p;
+            dv2[h] = p * (dp[i] - dvv[u][x]);
+          }
+          pk[e2] = pack_bf16x2(pv[0], pv[1]);
+          dk4[e2] = pack_bf16x2(dv2[0], dv2[1]);
+        }
+        pb[kk] = __builtin_bit_cast(bf16x8, pk);
+        sb[kk] = __builtin_bit_cast(bf16x8, dk4);
       }
-      pb[kk] = __builtin_bit_cast(bf16x8, pk);
-      sb[kk] = __builtin_bit_cast(bf16x8, dk4);
-    }
+    };
+    if (all_seen)
+      p_ds(std::true_type{});
+    else
+      p_ds(std::false_type{});
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
