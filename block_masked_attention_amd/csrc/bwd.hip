@@ -24,6 +24,7 @@
 
 #include <type_traits>
 
+#include "attn_index.h"
 #include "common.h"
 #include "geometry.h"
 #include "internal.h"
@@ -151,37 +152,55 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdArgs a) {
   const uint16_t* kbase = a.k + kvoff;
   const uint16_t* vbase = a.v + kvoff;
 
-  const int k_row = ql * D;
-  const int k_swz = swz<D>(ql) & (CPR - 1);
-  int t_lo[DT], t_hi[DT];   // transpose-read offsets: rows 4*hb + j/4 and 8 further
+  // The K and V tiles of a stage use the forward's LDS layout (fwd_off in
+  // attn_index.h), so every operand address is a lane constant plus a
+  // compile-time offset.  S^T / dP^T operand (key 32 sub + ql, chunk
+  // 2 ks + hb): kl[ks % 2] + 256 (ks - ks % 2) + 64 D sub bytes.  K^T operand
+  // of dQ^T (transpose read): lane (gi = lane / 16, j = lane % 16) reads 4
+  // values at column 32 dt + 16 (gi % 2) + 4 (j % 4) of key 32 sub + 16 kk +
+  // 4 hb + j / 4 (lo) and of the key 8 further (hi), at kt_lo (kt_hi) +
+  // 512 dt + 32 D (2 sub + kk).
+  const int kl0 = fwd_off<D>(ql, hb), kl1 = fwd_off<D>(ql, 2 + hb);
+  int kt_lo, kt_hi;
   {
     const int j = lane & 15, gi = lane >> 4;
-    const int r = 4 * hb + (j >> 2);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int dcol = 32 * dt + 16 * (gi & 1) + 4 * (j & 3);
-      t_lo[dt] = chunk_off<D>(r, dcol >> 3) + (dcol & 7);
-      t_hi[dt] = chunk_off<D>(r + 8, dcol >> 3) + (dcol & 7);
-    }
+    const int r = 4 * hb + (j >> 2), c = 2 * (gi & 1) + ((j & 3) >> 1);
+    kt_lo = fwd_off<D>(r, c) + 8 * (j & 1);
+    kt_hi = fwd_off<D>(r + 8, c) + 8 * (j & 1);
   }
 
   // Tile j straight from global memory into stage st (no registers): lane i
-  // of a wavefront's load lands 16 bytes at its slot of a contiguous 1 KB
-  // run, so it loads the chunk the permuted layout puts there.
+  // of a wavefront's load fills bytes 1024 run + 16 i of the tile, so it
+  // loads the key and chunk fwd_at names there, from the tile's first key
+  // row (a uniform base in SGPRs) plus a 32-bit lane offset; in a short
+  // tile, keys past t1 - 1 repeat key t1 - 1 (finite data the masks never
+  // let through).
   constexpr int DJ = TCH >= NT ? TCH / NT : 1;   // loads per wavefront per matrix
+  constexpr bool ALL_RUNS = TCH / 64 >= NW * DJ;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  int d_row[DJ];
+  unsigned d_off[DJ];
+#pragma unroll
+  for (int q = 0; q < DJ; ++q) {
+    int r, c;
+    fwd_at<D>(1024 * (w * DJ + q) + 16 * lane, r, c);
+    d_row[q] = r;
+    d_off[q] = (unsigned)(r * 2 * D + c * 16);
+  }
   auto issue = [&](int j, uint16_t* st) {
     int t0, t1;
     tile(j, t0, t1);
+    const uint16_t* kb = kbase + (size_t)t0 * D;
+    const uint16_t* vb = vbase + (size_t)t0 * D;
+    const int last = t1 - t0 - 1;
+    const unsigned mk = lds_addr(st), mv = lds_addr(st + TE);
 #pragma unroll
     for (int q = 0; q < DJ; ++q) {
-      const int run = w * DJ + q;
-      if (run * 64 < TCH) {
-        const int pos = run * 64 + lane;
-        const int r = pos / CPR, c = (pos % CPR) ^ (swz<D>(pos / CPR) & (CPR - 1));
-        const size_t off = (size_t)imin(t0 + r, t1 - 1) * D + 8 * c;
-        uint16_t* dst = st + run * 64 * 8;
-        lds_dma16(kbase + off, dst);
-        lds_dma16(vbase + off, dst + TE);
+      const int run = wu * DJ + q;
+      if (ALL_RUNS || run * 64 < TCH) {
+        const unsigned off = d_off[q] - (unsigned)((d_row[q] - imin(d_row[q], last)) * 2 * D);
+        lds_dma16_sa(kb, off, mk + run * 1024);
+        lds_dma16_sa(vb, off, mv + run * 1024);
       }
     }
   };
@@ -207,15 +226,15 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdArgs a) {
 
   // S^T and dP^T of one 32-key subtile
   auto sdp_sub = [&](const uint16_t* st, int sub, f32x16& sv, f32x16& dp) {
-    const uint16_t* kr = st + 32 * sub * D + k_row;
-    const uint16_t* vr = st + TE + 32 * sub * D + k_row;
+    const char* kr = (const char*)st + sub * 64 * D;
+    const char* vr = kr + 2 * TE;
     sv = f32x16{};
     dp = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      const int co = 8 * ((2 * ks + hb) ^ k_swz);
-      sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(kr + co), qreg[ks], sv, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vr + co), dreg[ks], dp, 0, 0, 0);
+      const int o = 256 * (ks & ~1) + ((ks & 1) ? kl1 : kl0);
+      sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(kr + o), qreg[ks], sv, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vr + o), dreg[ks], dp, 0, 0, 0);
     }
   };
   // dS^T of the subtile (keys [e0, e1); every pair allowed when full), then
@@ -242,13 +261,15 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdArgs a) {
       }
       dsb[kk] = __builtin_bit_cast(bf16x8, pk);
     }
+    unsigned b_lo = lds_addr(st) + kt_lo, b_hi = lds_addr(st) + kt_hi;
+    asm volatile("" : "+v"(b_lo), "+v"(b_hi));
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const uint16_t* kt = st + 16 * (2 * sub + kk) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const s16x4 lo = lds_read_tr(kt + t_lo[dt]);
-        const s16x4 hi = lds_read_tr(kt + t_hi[dt]);
+        const unsigned kt = (2 * sub + kk) * 32 * D + dt * 512;
+        const s16x4 lo = lds_read_tr_at(b_lo + kt);
+        const s16x4 hi = lds_read_tr_at(b_hi + kt);
         const bf16x8 kop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, dsb[kk], acc[dt], 0, 0, 0);
       }
