@@ -23,18 +23,18 @@ pytestmark = pytest.mark.gpu
 bda = pytest.importorskip("block_masked_attention_amd")
 
 
-def _gpu_commit(logits, masked, tokens, tau, k_min):
+def _gpu_commit(logits, masked, tokens, tau, k_min, workspace=None):
     t = tokens.clone().to(dev())
     m = masked.clone().to(dev())
-    bda.commit(logits.to(dev()), t, m, tau, k_min)
+    bda.commit(logits.to(dev()), t, m, tau, k_min, workspace=workspace)
     torch.cuda.synchronize()
     return t.cpu(), m.cpu()
 
 
-def _check(logits, masked, tau, k_min, what):
+def _check(logits, masked, tau, k_min, what, workspace=None):
     tokens = torch.full(masked.shape, -1, dtype=torch.int64)
     rt, rm, info = oracle.commit(logits, masked.numpy(), tokens.numpy(), tau, k_min)
-    gt, gm = _gpu_commit(logits, masked, tokens, tau, k_min)
+    gt, gm = _gpu_commit(logits, masked, tokens, tau, k_min, workspace)
     assert np.array_equal(gm.numpy(), rm), f"{what}: commit masks differ"
     assert np.array_equal(gt.numpy(), rt), f"{what}: committed tokens differ"
     return rt, rm, info
@@ -130,6 +130,31 @@ def test_commit_ties():
     rt, rm, _ = _check(lg.to(torch.bfloat16), masked, 0.99, 1, "ties")
     assert rt[0, 0] == 5 and rm[0].tolist() == [0, 1, 1]
     assert rt[1, 0] == 131071 or rm[1, 0] == 1
+
+
+def test_commit_workspace_any_contents_and_reuse():
+    """The workspace needs no initial contents: filled with constant or
+    random bytes before the first call, then reused by calls over fewer
+    groups, every call matches the oracle."""
+    G, R, V = 6, 28, 40000
+    ws = torch.empty(bda.lib.bda_commit_workspace_bytes(G, R, V), dtype=torch.uint8, device=dev())
+    g = torch.Generator().manual_seed(77)
+    fills = [lambda: ws.fill_(0xFF), lambda: ws.fill_(0xAB),
+             lambda: ws.copy_(torch.randint(0, 256, ws.shape, generator=g, dtype=torch.uint8).to(dev()))]
+    for i, fill in enumerate(fills):
+        fill()
+        for G1 in (G, 3, 1):
+            masked = (torch.rand(G1, R, generator=g) < 0.8).to(torch.uint8)
+            tokens = torch.full((G1, R), -1, dtype=torch.int64)
+            for attempt in range(16):
+                logits = _uniform(G1, R, V, seed=100 * i + 10 * G1 + attempt, dtype=torch.bfloat16)
+                _, _, info = oracle.commit(logits, masked.numpy(), tokens.numpy(), 0.3, 2)
+                if not _close_rows(info, masked.numpy(), 0.3, 2):
+                    break
+            else:
+                raise AssertionError("no seed left the guard band")
+            say(f"[commit workspace] fill {i} G={G1}")
+            _check(logits, masked, 0.3, 2, f"fill {i} G={G1}", workspace=ws)
 
 
 def test_commit_noop_and_errors():
