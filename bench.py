@@ -560,7 +560,9 @@ def secondary(bda, synth, torch, dev, args):
 def canvas_graph(bda, synth, torch, dev, iters):
     """One denoise step of the multimodal canvas (B=2, 28-row active block,
     threshold 0.9, at least one commit) as eager launches and as one HIP
-    graph replay, beside the HBM floors of its attention and commit; then
+    graph replay, beside the HBM floors of its attention and commit (the
+    step with row statistics and commit from one pass over the logits, and
+    for comparison with the two as separate calls); then
     the whole canvas run block by block with the graph (the host reads the
     commit mask after each step to move to the next block), reporting the
     steps it took against the 48-step budget."""
@@ -602,6 +604,15 @@ def canvas_graph(bda, synth, torch, dev, iters):
         bda.attn_fwd_varlen(x["q"], kc, vc, kl, "decode", nb, out=x["out"], workspace=x["ws_a"])
 
     def step(x, nb):
+        # the statistics and the commit from one pass over the logits
+        bda.kv_append(kc, vc, x["kb"], x["vb"], kl)
+        attention(x, nb)
+        bda.row_stats_commit(x["logits"], x["tokens"], x["masked"], 0.9, 1, workspace=x["ws_c"],
+                             out=(x["conf"], x["am"], x["ent"], x["mean"]))
+        bda.adaptive_stop(x["am"], x["prev"], x["stable"], x["frozen"], x["mean"], 1, 0.005, n_frozen=x["nfz"])
+
+    def step_separate(x, nb):
+        # the same step with the statistics and the commit as two calls
         bda.kv_append(kc, vc, x["kb"], x["vb"], kl)
         attention(x, nb)
         bda.row_stats(x["logits"], workspace=x["ws_s"], out=(x["conf"], x["am"], x["ent"], x["mean"]))
@@ -637,6 +648,9 @@ def canvas_graph(bda, synth, torch, dev, iters):
         x["masked"].fill_(1)
 
     t_eager, _ = time_launches(lambda i: step(x, n), iters, 5, pre=reset)
+    t_eager_sep, _ = time_launches(lambda i: step_separate(x, n), iters, 5, pre=reset)
+    g_sep = graph_of(n, step_separate)
+    t_graph_sep, _ = time_launches(lambda i: g_sep.replay(), iters, 5, pre=reset)
     g_step = graph_of(n, step)
     t_graph, _ = time_launches(lambda i: g_step.replay(), iters, 5, pre=reset)
     t_graph_host, _ = time_launches(lambda i: g_step.replay(), iters, 5, pre=reset, queue=False)
@@ -646,7 +660,7 @@ def canvas_graph(bda, synth, torch, dev, iters):
     L0 = synth.PREFIX + n
     att_bytes = B * Hq * n * d * 2 * 2 + B * Hkv * L0 * d * 2 * 2
     com_bytes = B * n * V * 2
-    floor = (att_bytes + 2 * com_bytes + B * Hkv * n * d * 2 * 2) / PEAK_HBM_GBS / 1e3
+    floor = (att_bytes + com_bytes + B * Hkv * n * d * 2 * 2) / PEAK_HBM_GBS / 1e3   # logits read once
 
     # the whole canvas: blocks of 28 (a last one of 4) in lockstep over the batch
     kl.fill_(synth.PREFIX)
@@ -670,6 +684,8 @@ def canvas_graph(bda, synth, torch, dev, iters):
     return {"B": B, "n": n, "kv_len_first_block": L0, "V": V,
             "us_per_step_eager": round(t_eager * 1e3, 2), "us_per_step_graph": round(t_graph * 1e3, 2),
             "us_per_step_graph_as_issued": round(t_graph_host * 1e3, 2),
+            "us_per_step_eager_separate_stats_commit": round(t_eager_sep * 1e3, 2),
+            "us_per_step_graph_separate_stats_commit": round(t_graph_sep * 1e3, 2),
             "attention_us_graph": round(t_att_graph * 1e3, 2), "attention_us_eager": round(t_att_eager * 1e3, 2),
             "attention_floor_us": round(att_bytes / PEAK_HBM_GBS / 1e3, 2),
             "step_hbm_floor_us": round(floor, 2),

@@ -28,6 +28,7 @@ _ENTRY_POINTS = (
     "bda_attn_fwd_lse", "bda_attn_bwd", "bda_attn_bwd_workspace_bytes", "bda_sprint_prune",
     "bda_sprint_workspace_bytes", "bda_sprint_kept_count", "bda_attn_fwd_varlen", "bda_kv_append",
     "bda_verify_crop", "bda_commit_entropy", "bda_commit_entropy_workspace_bytes", "bda_adaptive_stop",
+    "bda_row_stats_commit", "bda_row_stats_commit_workspace_bytes",
 )
 
 
@@ -79,6 +80,10 @@ def _load():
     L.bda_row_stats.restype = I
     L.bda_row_stats_workspace_bytes.argtypes = [I, I, I]
     L.bda_row_stats_workspace_bytes.restype = S
+    L.bda_row_stats_commit.argtypes = [P, I, P, P, F, I, P, P, P, P, I, I, I, P, S, P]
+    L.bda_row_stats_commit.restype = I
+    L.bda_row_stats_commit_workspace_bytes.argtypes = [I, I, I]
+    L.bda_row_stats_commit_workspace_bytes.restype = S
     L.bda_sprint_prune.argtypes = [P, P, P, P, F, F, F, P, P, I, P, P, P, I, I, I, I, P, S, P]
     L.bda_sprint_prune.restype = I
     L.bda_sprint_workspace_bytes.argtypes = [I, I]
@@ -430,6 +435,46 @@ def row_stats(logits, masked=None, workspace=None, out=None):
                            G, R, V, _ptr(ws), need, _stream(dev))
     if rc:
         raise BdaError(rc, "bda_row_stats")
+    return conf, am, ent, mean
+
+
+def row_stats_commit(logits, tokens, masked, threshold: float, k_min: int, workspace=None, out=None):
+    """Row statistics of every row and the confidence commit of the masked
+    rows from one pass over logits [G,R,V] (bf16 or fp32): the results of
+    row_stats(logits) and then commit(logits, tokens, masked, threshold,
+    k_min).  ``tokens`` int64 [G,R] and ``masked`` uint8 [G,R] are updated in
+    place.  Returns (conf, argmax, entropy, mean_entropy), written into
+    ``out`` when given (four tensors as for row_stats)."""
+    if logits.dim() != 3:
+        raise ValueError("logits must be [G, R, V]")
+    G, R, V = logits.shape
+    dt = {torch.bfloat16: BF16, torch.float32: F32}.get(logits.dtype)
+    if dt is None:
+        raise ValueError("logits must be bfloat16 or float32")
+    if tokens.dtype != torch.int64 or masked.dtype != torch.uint8:
+        raise ValueError("tokens int64, masked uint8")
+    if tuple(tokens.shape) != (G, R) or tuple(masked.shape) != (G, R):
+        raise ValueError("tokens/masked must be [G, R]")
+    dev = _check_dev(logits, tokens, masked)
+    if out is not None:
+        conf, am, ent, mean = out
+        for t, dt_, shp in ((conf, torch.float32, (G, R)), (am, torch.int64, (G, R)), (ent, torch.float32, (G, R)),
+                            (mean, torch.float32, (G,))):
+            if t.dtype != dt_ or tuple(t.shape) != shp or not t.is_contiguous() or t.device != dev:
+                raise ValueError("out tensors must be contiguous conf/entropy float32 [G,R], argmax int64 [G,R], "
+                                 "mean float32 [G] on the logits' device")
+    else:
+        conf = torch.empty((G, R), dtype=torch.float32, device=dev)
+        am = torch.empty((G, R), dtype=torch.int64, device=dev)
+        ent = torch.empty((G, R), dtype=torch.float32, device=dev)
+        mean = torch.empty(G, dtype=torch.float32, device=dev)
+    need = int(lib.bda_row_stats_commit_workspace_bytes(G, R, V))
+    ws = _workspace(need, dev, workspace)
+    rc = lib.bda_row_stats_commit(_ptr(logits), dt, _ptr(tokens), _ptr(masked), float(threshold), int(k_min),
+                                  _ptr(conf), _ptr(am), _ptr(ent), _ptr(mean), G, R, V, _ptr(ws), need,
+                                  _stream(dev))
+    if rc:
+        raise BdaError(rc, "bda_row_stats_commit")
     return conf, am, ent, mean
 
 

@@ -409,6 +409,43 @@ int bda_row_stats(const void* logits, int dtype, const uint8_t* masked, float* c
   return ok();
 }
 
+size_t bda_row_stats_commit_workspace_bytes(int G, int R, int V) { return bda_commit_workspace_bytes(G, R, V); }
+
+int bda_row_stats_commit(const void* logits, int dtype, int64_t* tokens, uint8_t* masked, float threshold,
+                         int k_min, float* conf, int64_t* argmax_out, float* entropy, float* mean_entropy, int G,
+                         int R, int V, void* workspace, size_t ws_bytes, void* stream) {
+  if (int e = check_logits(logits, dtype, G, R, V, "G")) return e;
+  if (k_min < 0) return fail(BDA_EINVAL, "k_min must be >= 0");
+  if (isnan(threshold)) return fail(BDA_EINVAL, "threshold is NaN");
+  if (G == 0) return ok();
+  const size_t rows = (size_t)G * R;
+  if (rows && (!tokens || !masked)) return fail(BDA_EINVAL, "tokens and masked must be non-NULL");
+  const size_t lbytes = rows * V * (dtype == BDA_BF16 ? 2 : 4);
+  struct Buf {
+    const void* p;
+    size_t n;
+  } bufs[] = {{logits, lbytes},       {tokens, rows * 8},  {masked, rows},          {conf, rows * 4},
+              {argmax_out, rows * 8}, {entropy, rows * 4}, {mean_entropy, (size_t)G * 4}};
+  constexpr int NB = sizeof(bufs) / sizeof(bufs[0]);
+  for (int i = 0; i < NB; ++i)
+    for (int j = i + 1; j < NB; ++j)
+      if (bufs[i].p && bufs[j].p && overlap(bufs[i].p, bufs[i].n, bufs[j].p, bufs[j].n))
+        return fail(BDA_EINVAL, "logits, tokens, masked and the statistics outputs must not overlap");
+  bda::CommitPlan p;
+  bda::commit_make_plan(G, R, V, dtype, &p);
+  if (!workspace || ws_bytes < p.ws_bytes)
+    return fail(BDA_EWORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_bytes,
+                workspace ? ws_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(BDA_EINVAL, "workspace must be 16-byte aligned");
+  for (int i = 0; i < NB; ++i)
+    if (bufs[i].p && overlap(workspace, p.ws_bytes, bufs[i].p, bufs[i].n))
+      return fail(BDA_EINVAL, "workspace overlaps a tensor argument");
+  hipError_t e = bda::stats_commit_launch(p, logits, tokens, masked, threshold, k_min, conf, argmax_out, entropy,
+                                          mean_entropy, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BDA_EHIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int bda_sprint_kept_count(int n_image, int n_text, float r_img, float r_text) {
   if (n_image < 0 || n_text < 0 || !(r_img >= 0.f && r_img <= 1.f) || !(r_text >= 0.f && r_text <= 1.f)) return -1;
   return bda::sprint_keep(n_image, r_img) + bda::sprint_keep(n_text, r_text);

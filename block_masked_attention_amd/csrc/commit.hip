@@ -366,19 +366,44 @@ __device__ __forceinline__ int block_sum(int x, int* red) {
   return s;
 }
 
+__device__ __forceinline__ float block_sum_f(float x, float* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int w = 0; w < kCommitThreads / 64; ++w) s += red[w];
+  __syncthreads();
+  return s;
+}
+
+// Row statistics written beside a commit (STATS = true); any may be NULL.
+struct StatsOut {
+  float* conf;
+  int64_t* argmax;
+  float* entropy;
+  float* mean_entropy;
+};
+
 // One workgroup per group g.  Row results (p, argmax, flag) live in LDS
 // when R <= kFinRows, else in the workspace scratch rowp/rowa/rowf [G*R].
 // Each row's mask byte and chunk partials are loaded together (partials of
 // unmasked rows are stale and ignored), so the critical path holds one
-// round trip to memory.
+// round trip to memory.  STATS: the partials are those of every row (with
+// T), and each row's confidence, argmax and entropy and the group's mean
+// entropy are written as the row statistics kernel below writes them (same
+// expressions, same summation order).
 constexpr int kFinRows = 2048;
 
-template <bool IN_LDS>
+template <bool IN_LDS, bool STATS>
 __global__ __launch_bounds__(kCommitThreads) void commit_finalize_kernel(
     const Partial* __restrict__ part, int n_chunks, int64_t* __restrict__ tokens,
     uint8_t* __restrict__ masked, float threshold, int k_min, int R, float* __restrict__ rowp,
-    int* __restrict__ rowa, uint8_t* __restrict__ rowf) {
+    int* __restrict__ rowa, uint8_t* __restrict__ rowf, const StatsOut so) {
   __shared__ int red[2][kCommitThreads / 64];
+  __shared__ float redf[kCommitThreads / 64];
+  __shared__ int redi[kCommitThreads / 64];
   __shared__ float lp[IN_LDS ? kFinRows : 1];
   __shared__ int la[IN_LDS ? kFinRows : 1];
   __shared__ uint8_t lf[IN_LDS ? kFinRows : 1];
@@ -388,12 +413,14 @@ __global__ __launch_bounds__(kCommitThreads) void commit_finalize_kernel(
   int* ra = IN_LDS ? la : rowa + base;
   uint8_t* rf = IN_LDS ? lf : rowf + base;
   int nmask = 0, npass = 0;
+  float hsum = 0.f;
+  int cnt = 0;
   const int CH = lanes_per_row(n_chunks), ci = tid % CH;
   for (int r0 = 0; r0 < R; r0 += kCommitThreads / CH) {
     const int r = r0 + tid / CH;
     const bool in = r < R;
     const uint8_t mk = in && ci == 0 ? masked[base + r] : 0;
-    const Stat s = row_stat_lanes(part, base + r, in, ci, CH, n_chunks, kWithZ);
+    const Stat s = row_stat_lanes(part, base + r, in, ci, CH, n_chunks, STATS ? kWithZT : kWithZ);
     if (in && ci == 0) {
       const float p = 1.f / s.z;
       const uint8_t f = mk ? (p > threshold ? 2 : 1) : 0;
@@ -402,7 +429,20 @@ __global__ __launch_bounds__(kCommitThreads) void commit_finalize_kernel(
       rf[r] = f;
       nmask += f != 0;
       npass += f == 2;
+      if constexpr (STATS) {
+        const float h = logf(s.z) - s.t / s.z;
+        if (so.conf) so.conf[base + r] = 1.f / s.z;
+        if (so.argmax) so.argmax[base + r] = s.a;
+        if (so.entropy) so.entropy[base + r] = h;
+        hsum += h;
+        cnt += 1;
+      }
     }
+  }
+  if constexpr (STATS) {
+    hsum = block_sum_f(hsum, redf);
+    cnt = block_sum(cnt, redi);
+    if (tid == 0 && so.mean_entropy) so.mean_entropy[g] = cnt > 0 ? hsum / (float)cnt : 0.f;
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -472,18 +512,6 @@ __global__ __launch_bounds__(kCommitThreads) void verify_finalize_kernel(
     accept[b] = m;
     if (kv_len != nullptr) kv_len[b] = min(kv_len[b] + m, kv_cap);   // keep the accepted drafts' rows
   }
-}
-
-__device__ __forceinline__ float block_sum_f(float x, float* red) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  float s = 0.f;
-#pragma unroll
-  for (int w = 0; w < kCommitThreads / 64; ++w) s += red[w];
-  __syncthreads();
-  return s;
 }
 
 // One workgroup per group: per selected row the confidence 1/Z, the argmax
@@ -739,11 +767,36 @@ hipError_t commit_launch(const CommitPlan& p, const void* logits, int64_t* token
   hipError_t e = launch_stream<kWithZ>(p, logits, masked, part, st);
   if (e != hipSuccess) return e;
   if (p.R <= kFinRows)
-    hipLaunchKernelGGL(commit_finalize_kernel<true>, dim3(p.G), dim3(kCommitThreads), 0, st, part,
-                       p.n_chunks, tokens, masked, threshold, k_min, p.R, rowp, rowa, rowf);
+    hipLaunchKernelGGL((commit_finalize_kernel<true, false>), dim3(p.G), dim3(kCommitThreads), 0, st, part,
+                       p.n_chunks, tokens, masked, threshold, k_min, p.R, rowp, rowa, rowf, StatsOut{});
   else
-    hipLaunchKernelGGL(commit_finalize_kernel<false>, dim3(p.G), dim3(kCommitThreads), 0, st, part,
-                       p.n_chunks, tokens, masked, threshold, k_min, p.R, rowp, rowa, rowf);
+    hipLaunchKernelGGL((commit_finalize_kernel<false, false>), dim3(p.G), dim3(kCommitThreads), 0, st, part,
+                       p.n_chunks, tokens, masked, threshold, k_min, p.R, rowp, rowa, rowf, StatsOut{});
+  return hipGetLastError();
+}
+
+hipError_t stats_commit_launch(const CommitPlan& p, const void* logits, int64_t* tokens, uint8_t* masked,
+                               float threshold, int k_min, float* conf, int64_t* argmax_out, float* entropy,
+                               float* mean_entropy, void* ws, hipStream_t st) {
+  if (p.G == 0) return hipSuccess;
+  Partial* part;
+  float* rowp;
+  int* rowa;
+  uint8_t* rowf;
+  carve(p, ws, &part, &rowp, &rowa, &rowf);
+  (void)hipGetLastError();
+  if (p.R > 0) {
+    // every row is streamed: the statistics cover all rows, the commit the masked ones
+    hipError_t e = launch_stream<kWithZT>(p, logits, nullptr, part, st);
+    if (e != hipSuccess) return e;
+  }
+  const StatsOut so{conf, argmax_out, entropy, mean_entropy};
+  if (p.R <= kFinRows)
+    hipLaunchKernelGGL((commit_finalize_kernel<true, true>), dim3(p.G), dim3(kCommitThreads), 0, st, part,
+                       p.n_chunks, tokens, masked, threshold, k_min, p.R, rowp, rowa, rowf, so);
+  else
+    hipLaunchKernelGGL((commit_finalize_kernel<false, true>), dim3(p.G), dim3(kCommitThreads), 0, st, part,
+                       p.n_chunks, tokens, masked, threshold, k_min, p.R, rowp, rowa, rowf, so);
   return hipGetLastError();
 }
 

@@ -49,6 +49,9 @@ hipError_t commit_launch(const CommitPlan& p, const void* logits, int64_t* token
 hipError_t stats_launch(const CommitPlan& p, const void* logits, const uint8_t* masked, float* conf,
                         int64_t* argmax_out, float* entropy, float* mean_entropy, void* ws,
                         hipStream_t st);
+hipError_t stats_commit_launch(const CommitPlan& p, const void* logits, int64_t* tokens, uint8_t* masked,
+                               float threshold, int k_min, float* conf, int64_t* argmax_out, float* entropy,
+                               float* mean_entropy, void* ws, hipStream_t st);
 hipError_t verify_launch(const CommitPlan& p, const void* logits, const int64_t* drafts,
                          int64_t* argmax_out, int32_t* accept, int32_t* kv_len, int kv_cap, void* ws,
                          hipStream_t st);

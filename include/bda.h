@@ -146,7 +146,8 @@ size_t bda_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int bl
 /*
  * Confidence commit ([LLaDA] SPRINT; [DGemma] Schedulers; [VLM-8B]).
  * logits: [G, R, V] of dtype BDA_BF16 or BDA_F32 (G independent groups, e.g.
- *   sequences; R canvas positions; V vocabulary).  Values must be finite.
+ *   sequences; R canvas positions; V vocabulary).  Values are finite or
+ *   -inf (a banned token, probability 0); every row holds a finite value.
  * masked: [G, R] uint8, 1 = position still masked; updated in place.
  * tokens: [G, R] int64; written only at the positions this call commits.
  * For each group, among masked rows: c_r = largest softmax probability of
@@ -208,7 +209,7 @@ int bda_verify_crop(const void* logits, int dtype, const int64_t* drafts, int64_
  * Entropy-bound commit ([DGemma] Schedulers: the entropy-bound scheduler
  * commits the lowest-entropy positions whose joint entropy stays within a
  * bound, so that roughly independent tokens are accepted together).
- * logits [G, R, V] (BDA_BF16 or BDA_F32, finite); masked [G, R] uint8 and
+ * logits [G, R, V] (BDA_BF16 or BDA_F32, finite or -inf as for bda_commit); masked [G, R] uint8 and
  * tokens [G, R] int64, updated in place as by bda_commit.  For every masked
  * row: H = entropy in nats of softmax(logits / temperature), a = lowest index
  * of the largest logit.  Per group, the masked rows ordered by (H ascending,
@@ -253,7 +254,8 @@ int bda_adaptive_stop(const int64_t* argmax, int64_t* prev_argmax, int32_t* stab
  * once its argmax is stable and its mean per-token entropy is below a
  * confidence threshold; [DGemma] Schedulers: the entropy-bound scheduler
  * commits the lowest-entropy positions) and the SPRINT confidence ([LLaDA]).
- * logits: [G, R, V] of dtype BDA_BF16 or BDA_F32; values must be finite.
+ * logits: [G, R, V] of dtype BDA_BF16 or BDA_F32; values finite or -inf (a
+ *   banned token: probability 0, no entropy term), at least one finite per row.
  * masked: [G, R] uint8 or NULL.  When given, only rows with masked != 0 are
  *   computed (outputs of the other rows are left untouched); NULL = all rows.
  * For each computed row, with p = softmax(row) at temperature 1:
@@ -268,6 +270,25 @@ int bda_row_stats(const void* logits, int dtype, const uint8_t* masked, float* c
                   int64_t* argmax, float* entropy, float* mean_entropy, int G, int R, int V,
                   void* workspace, size_t ws_bytes, void* stream);
 size_t bda_row_stats_workspace_bytes(int G, int R, int V);
+
+/*
+ * Row statistics and the confidence commit of one denoising step, from one
+ * pass over its logits ([DGemma] "Adaptive stopping" and "Schedulers": each
+ * step's logits feed both the stopping test and the commit; [LLaDA]
+ * SPRINT).  Computes what bda_row_stats(logits, masked = NULL, conf, argmax,
+ * entropy, mean_entropy) and then bda_commit(logits, tokens, masked,
+ * threshold, k_min) compute: the statistics cover every row, the commit the
+ * rows with masked != 0 (tokens and masked updated as bda_commit does).  The
+ * logits are read once instead of twice.  Any of conf, argmax, entropy and
+ * mean_entropy may be NULL (not written); with R = 0 mean_entropy is 0.  No
+ * two of logits, tokens, masked and the outputs may overlap.
+ * workspace: at least bda_row_stats_commit_workspace_bytes(G, R, V) bytes.
+ */
+int bda_row_stats_commit(const void* logits, int dtype, int64_t* tokens, uint8_t* masked,
+                         float threshold, int k_min, float* conf, int64_t* argmax,
+                         float* entropy, float* mean_entropy, int G, int R, int V,
+                         void* workspace, size_t ws_bytes, void* stream);
+size_t bda_row_stats_commit_workspace_bytes(int G, int R, int V);
 
 /*
  * SPRINT sparse prefix retention ([LLaDA] "SPRINT"): prune the clean KV

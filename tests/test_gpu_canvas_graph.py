@@ -4,8 +4,9 @@ The step of [DGemma] "정적 캐시 및 컴파일" (a static cache, so the decod
 step can be captured) with the stopping rule of "적응형 중단": write the
 active block's K/V rows into the cache; DECODE attention of the block's
 queries over the cache; row statistics (confidence, argmax, entropy and the
-group mean entropy); the adaptive-stop update; the confidence commit.
-Seeded queries, rows and logits stand in for the model.
+group mean entropy); the adaptive-stop update; the confidence commit.  The
+statistics and the commit run as two calls or as the one call that reads
+the logits once.  Seeded queries, rows and logits stand in for the model.
 
 The step is captured once and replayed for several steps, with fresh inputs
 copied in and other work run eagerly between the replays.  Every replay is
@@ -65,12 +66,17 @@ class Canvas:
         self.vb.copy_(vb)
         self.logits.copy_(lg)
 
-    def run(self):
+    def run(self, fused):
         bda.kv_append(self.kc, self.vc, self.kb, self.vb, self.kl)
         bda.attn_fwd_varlen(self.q, self.kc, self.vc, self.kl, "decode", n, out=self.out, workspace=self.ws_a)
-        bda.row_stats(self.logits, workspace=self.ws_s, out=(self.conf, self.am, self.ent, self.mean))
-        bda.adaptive_stop(self.am, self.prev, self.stable, self.frozen, self.mean, 1, 0.005, n_frozen=self.nfz)
-        bda.commit(self.logits, self.tokens, self.masked, 0.9, 1, workspace=self.ws_c)
+        stats = (self.conf, self.am, self.ent, self.mean)
+        if fused:      # statistics and commit from one pass over the logits
+            bda.row_stats_commit(self.logits, self.tokens, self.masked, 0.9, 1, workspace=self.ws_c, out=stats)
+            bda.adaptive_stop(self.am, self.prev, self.stable, self.frozen, self.mean, 1, 0.005, n_frozen=self.nfz)
+        else:
+            bda.row_stats(self.logits, workspace=self.ws_s, out=stats)
+            bda.adaptive_stop(self.am, self.prev, self.stable, self.frozen, self.mean, 1, 0.005, n_frozen=self.nfz)
+            bda.commit(self.logits, self.tokens, self.masked, 0.9, 1, workspace=self.ws_c)
 
     def snapshot(self):
         names = ("out", "conf", "am", "ent", "mean", "prev", "stable", "frozen", "nfz", "tokens", "masked")
@@ -86,7 +92,8 @@ def _same(a, b):
     return torch.equal(a, b)
 
 
-def test_canvas_step_graph_replays_match_eager():
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+def test_canvas_step_graph_replays_match_eager(fused):
     g = torch.Generator().manual_seed(31)
     kc0 = (torch.randn(B, Hkv, CAP, d, generator=g) * 0.5).to(torch.bfloat16)
     vc0 = (torch.randn(B, Hkv, CAP, d, generator=g) * 0.5).to(torch.bfloat16)
@@ -94,13 +101,13 @@ def test_canvas_step_graph_replays_match_eager():
     say(f"[canvas graph] B={B} n={n} cache {CAP} keys {synth.PREFIX + n} V={V}: warm-up launches")
     warm = Canvas(kc0, vc0)                    # first launches outside the capture
     warm.load(steps[0])
-    warm.run()
+    warm.run(fused)
     torch.cuda.synchronize()
     del warm
     gc, ec = Canvas(kc0, vc0), Canvas(kc0, vc0)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        gc.run()
+        gc.run(fused)
     torch.cuda.synchronize()
     spare = torch.randn(1 << 20, device=dev())
     for t in range(STEPS):
@@ -112,7 +119,7 @@ def test_canvas_step_graph_replays_match_eager():
         graph.replay()
         torch.cuda.synchronize()
         gs = gc.snapshot()
-        ec.run()
+        ec.run(fused)
         torch.cuda.synchronize()
         es = ec.snapshot()
         for key in gs:
