@@ -105,6 +105,13 @@ int main() {
                          nullptr) == BDA_EINVAL);
   EXPECT(bda_row_stats(q, 5, nullptr, nullptr, nullptr, nullptr, nullptr, 2, 4, 100, ws, 1 << 20, nullptr) ==
          BDA_EINVAL);
+  EXPECT(bda_row_stats_commit(q, 5, tok, msk, 0.9f, 1, nullptr, nullptr, nullptr, nullptr, 2, 4, 100, ws, 1 << 20,
+                              nullptr) == BDA_EINVAL);
+  EXPECT(bda_row_stats_commit(q, BDA_BF16, tok, msk, 0.9f, 1, nullptr, nullptr, nullptr, nullptr, 2, 4, 100, nullptr,
+                              0, nullptr) == BDA_EWORKSPACE);
+  EXPECT(bda_row_stats_commit(q, BDA_BF16, tok, msk, 0.9f, 1, (float*)q, nullptr, nullptr, nullptr, 2, 4, 100, ws,
+                              1 << 20, nullptr) == BDA_EINVAL);   // conf overlaps the logits
+  EXPECT(bda_row_stats_commit_workspace_bytes(2, 4, 100) == bda_commit_workspace_bytes(2, 4, 100));
   EXPECT(bda_adaptive_stop(tok, tok, (int32_t*)msk, msk, (const float*)ws, 2, 4, -1, 0.005f, nullptr, nullptr) ==
          BDA_EINVAL);
   EXPECT(bda_adaptive_stop(tok, tok, (int32_t*)msk, msk, (const float*)ws, 2, 4, 1, 0.005f, nullptr, nullptr) ==

@@ -126,6 +126,25 @@ def test_row_stats_validation():
     assert f(A, 0, None, ctypes.c_void_p((1 << 32) + 16), None, None, None, 1, 5, 10, Wp, need, None) == 1  # overlap
 
 
+def test_row_stats_commit_validation():
+    f = bda.lib.bda_row_stats_commit
+    T, M = ctypes.c_void_p(6 << 32), ctypes.c_void_p(7 << 32)
+    # logits, dtype, tokens, masked, threshold, k_min, conf, argmax, entropy, mean, G, R, V, ws, ws_bytes, stream
+    assert f(A, 0, T, M, 0.9, 1, None, None, None, None, 0, 5, 10, None, 0, None) == 0        # nothing to do
+    assert f(A, 3, T, M, 0.9, 1, None, None, None, None, 1, 5, 10, Wp, 1 << 20, None) == 1    # dtype
+    assert f(A, 0, T, M, float("nan"), 1, None, None, None, None, 1, 5, 10, Wp, 1 << 20, None) == 1
+    assert f(A, 0, T, M, 0.9, -1, None, None, None, None, 1, 5, 10, Wp, 1 << 20, None) == 1   # k_min
+    assert f(A, 0, None, M, 0.9, 1, None, None, None, None, 1, 5, 10, Wp, 1 << 20, None) == 1  # tokens
+    assert f(A, 0, T, M, 0.9, 1, None, None, None, None, 1, 5, 10, None, 0, None) == 3        # workspace
+    need = bda.lib.bda_row_stats_commit_workspace_bytes(1, 5, 10)
+    assert need == bda.lib.bda_commit_workspace_bytes(1, 5, 10) > 0
+    assert f(A, 0, T, M, 0.9, 1, None, None, None, None, 1, 5, 10, Wp, need - 1, None) == 3
+    assert f(A, 0, T, M, 0.9, 1, ctypes.c_void_p((1 << 32) + 16), None, None, None, 1, 5, 10, Wp, need,
+             None) == 1                                                                        # conf overlaps logits
+    assert f(A, 0, T, M, 0.9, 1, None, ctypes.c_void_p((7 << 32) + 2), None, None, 1, 5, 10, Wp, need,
+             None) == 1                                                                        # argmax overlaps masked
+
+
 def test_sprint_validation():
     f = bda.lib.bda_sprint_prune
     E, Fp, Gp = (ctypes.c_void_p(x << 32) for x in (6, 7, 8))
