@@ -299,22 +299,28 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdArgs a) {
     __builtin_amdgcn_s_waitcnt(0);               // Q, dO and the first tiles
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    // Two loops, not one with a branch per tile: with both paths in one
+    // loop body the compiler kept the dQ accumulators in two register sets
+    // and copied all 64 of them twice per tile.
 #pragma unroll 1
-    for (int j = 0; j < nt; ++j) {
+    for (int j = 0; j < nf; ++j) {
+      // clean-prefix tile every row sees: no classification, no branches
       if (issued < nt) issue(issued, stq(issued)), ++issued;
       const uint16_t* cur = stq(j);
-      if (j < nf) {
-        // clean-prefix tile every row sees: no classification, no branches
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-          f32x16 sv, dp;
-          sdp_sub(cur, sub, sv, dp);
-          grad_sub(cur, sub, 0, 0, true, sv, dp);
-        }
-      } else {
-        subtile(cur, j, 0);
-        subtile(cur, j, 1);
+      for (int sub = 0; sub < 2; ++sub) {
+        f32x16 sv, dp;
+        sdp_sub(cur, sub, sv, dp);
+        grad_sub(cur, sub, 0, 0, true, sv, dp);
       }
+      settle_for(j + 1, issued);
+    }
+#pragma unroll 1
+    for (int j = nf; j < nt; ++j) {
+      if (issued < nt) issue(issued, stq(issued)), ++issued;
+      const uint16_t* cur = stq(j);
+      subtile(cur, j, 0);
+      subtile(cur, j, 1);
       settle_for(j + 1, issued);
     }
   }
