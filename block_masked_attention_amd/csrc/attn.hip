@@ -65,6 +65,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
   constexpr int STAGE = 2 * TE;
   constexpr int KT = 2 * TE;                  // bytes of one K (or V) tile
   __shared__ __attribute__((aligned(16))) uint16_t smem[STAGES * STAGE];
+  // persistent walk: where wavefronts 4..7 stage an item's O (waves 0..3 use
+  // the ring stage of the item's last tile)
+  __shared__ __attribute__((aligned(16))) uint16_t oext[STAGES == 4 ? 4 * 32 * D : 8];
   // K tiles of the ring stages first, then the V tiles (all K operand reads
   // stay below 64 KB of the LDS base, within the reads' immediate offset)
   char* const sm = reinterpret_cast<char*>(smem);
@@ -502,7 +505,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
   };
 
   // ---- epilogue of the current item: lane (ql, hb) holds
-  // d = 32*dt + 8*(i/4) + 4*hb + (i%4)
+  // d = 32*dt + 8*(i/4) + 4*hb + (i%4).  The persistent walk (one output,
+  // no key split) sends O through oreg, its wavefront's 32 x D region of
+  // LDS: written in the accumulator layout with the 16-byte chunks of a row
+  // XOR-swizzled by the row, read back 16 bytes per lane so that each store
+  // writes whole rows (D / 8 lanes per row) instead of 16 bytes of 32 rows.
+  char* oreg = nullptr;
   auto finish = [&]() {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
@@ -520,7 +528,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
             u32x2 pk;
             pk[0] = pack_bf16x2(o[qb][dt][4 * i4] * inv, o[qb][dt][4 * i4 + 1] * inv);
             pk[1] = pack_bf16x2(o[qb][dt][4 * i4 + 2] * inv, o[qb][dt][4 * i4 + 3] * inv);
-            *(u32x2*)(op + 32 * dt + 8 * i4) = pk;
+            if constexpr (WALK == kWalkPersistent) {
+              const int c = 4 * dt + i4;   // 16-byte chunk of the row
+              *(u32x2*)(oreg + ql * (2 * D) + ((c ^ (ql & (CPR - 1))) << 4) + 8 * hb) = pk;
+            } else {
+              *(u32x2*)(op + 32 * dt + 8 * i4) = pk;
+            }
           }
         }
       } else {
@@ -539,6 +552,27 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
           pm[0] = m_run[qb] == -INFINITY ? -INFINITY : m_run[qb] * sl2;
           pm[1] = l_tot;
         }
+      }
+    }
+    if constexpr (WALK == kWalkPersistent) {
+      static_assert(NQB == 1 && NW == 8, "O staging: 8 wavefronts of 32 slots");
+      if (a.n_splits == 1) {
+        // lane (ql, either half) knows the output row of slot ql (-1: none)
+        const long long rowi = valid[0] ? (long long)attn_q_row(a, b, head[0], qrow[0]) : -1;
+        constexpr int RPI = 64 / CPR;   // rows per store instruction
+#pragma unroll
+        for (int k = 0; k < 32 / RPI; ++k) {
+          const int r = k * RPI + lane / CPR, c = lane % CPR;
+          const u32x4 x = *(const u32x4*)(oreg + r * (2 * D) + ((c ^ (r & (CPR - 1))) << 4));
+          const long long rr = __shfl(rowi, r);
+          if (rr >= 0) *(u32x4*)(a.out + (size_t)rr * D + 8 * c) = x;
+        }
+        // every wavefront has read its O back before the next item's first
+        // tile copy goes into the ring stage
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0) only
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
       }
     }
   };
@@ -843,6 +877,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
           settle();
         }
         sp += nt;
+      }
+      {
+        // the ring stage of the item's last tile is free until the next
+        // item's first step copies into it
+        const int ls = (sp - 1) & 3;
+        oreg = w < 4 ? (w < 2 ? kst(ls) : vst(ls)) + (w & 1) * (KT / 2)
+                     : reinterpret_cast<char*>(oext) + (w - 4) * (KT / 2);
       }
       finish();
     }

@@ -83,7 +83,8 @@ static bool g_stand_in = true;
 // boundary step nothing.  Fast step i of an item reads stream tiles i and
 // i + 1 (the next tile's K); a boundary step reads tile i, after waiting
 // for every load when it had nothing to issue.  Every step ends by waiting
-// for all loads but the newest, then the barrier.
+// for all loads but the newest, then the barrier.  After an item's last step
+// its epilogue uses the stage of that step's tile as scratch.
 static void ring_replay(const AttnIndex& a, const int32_t* kv_len, long long grid, const char* what) {
   for (long long wg = 0; wg < grid; ++wg) {
     std::vector<Geom> items;
@@ -134,6 +135,12 @@ static void ring_replay(const AttnIndex& a, const int32_t* kv_len, long long gri
         settle();
       }
       sp += gm.nt;
+      // the item's epilogue stages O in the ring stage of its last tile
+      // (waves 0..3) until a barrier that precedes the next step's issue:
+      // no issue since that tile may have gone into that stage
+      const long long last = sp - 1;
+      CHECK(last < 0 ? owner[3] == -1 : owner[last & 3] == issue_of[(size_t)last],
+            "%s: wg %lld: the stage of stream tile %lld was reissued before the item's epilogue", what, wg, last);
     }
   }
 }
