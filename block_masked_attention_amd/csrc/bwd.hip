@@ -325,9 +325,14 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdArgs a) {
     }
   }
 
-  // dq = scale * dQ^T; lane (ql, hb) holds d = 32*dt + 8*(i/4) + 4*hb + (i%4)
+  // dq = scale * dQ^T; lane (ql, hb) holds d = 32*dt + 8*(i/4) + 4*hb + (i%4).
+  // Through LDS (the ring, idle after the last step's barrier), so that each
+  // store writes whole rows rather than 16 bytes of 32 rows: the wavefront's
+  // 32 rows go into its 32 x D region in the accumulator layout, 16-byte
+  // chunks XOR-swizzled by the row, and come back 16 bytes per lane.
+  static_assert(NW * 32 * 2 * D <= NSQ * 2 * TE * 2, "dq staging exceeds the ring");
+  char* reg = reinterpret_cast<char*>(smem) + w * (32 * 2 * D);
   if (valid) {
-    uint16_t* op = a.dq + rowi * D + 4 * hb;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -335,8 +340,18 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdArgs a) {
         u32x2 pk;
         pk[0] = pack_bf16x2(acc[dt][4 * i4] * a.scale, acc[dt][4 * i4 + 1] * a.scale);
         pk[1] = pack_bf16x2(acc[dt][4 * i4 + 2] * a.scale, acc[dt][4 * i4 + 3] * a.scale);
-        *(u32x2*)(op + 32 * dt + 8 * i4) = pk;
+        const int c = 4 * dt + i4;   // 16-byte chunk of the row
+        *(u32x2*)(reg + ql * (2 * D) + ((c ^ (ql & (CPR - 1))) << 4) + 8 * hb) = pk;
       }
+  }
+  const long long ri = valid ? (long long)rowi : -1;   // lane (ql, either half): row of slot ql
+  constexpr int RPI = 64 / CPR;                       // rows per store instruction
+#pragma unroll
+  for (int k = 0; k < 32 / RPI; ++k) {
+    const int r = k * RPI + lane / CPR, c = lane % CPR;
+    const u32x4 x = *(const u32x4*)(reg + r * (2 * D) + ((c ^ (r & (CPR - 1))) << 4));
+    const long long rr = __shfl(ri, r);
+    if (rr >= 0) *(u32x4*)(a.dq + (size_t)rr * D + 8 * c) = x;
   }
 }
 
