@@ -57,6 +57,7 @@ SMALL = [
     ("decode", 1, 8, 2, 512, 128, 128),    # 8-wave persistent walk, items of full tiles only
     ("causal", 1, 8, 2, 256, 128, 129),    # last query tile (one row) sees all 256 keys
     ("decode", 1, 4, 1, 20, 128, 20),      # fewer keys than half a tile: one key group sees none
+    ("causal", 1, 4, 1, 2048, 128, 128),   # persistent walk with 8 key splits (partials, then the combine)
 ]
 
 
