@@ -105,6 +105,44 @@ def test_multi_item_elementwise(mode, B, Hq, Hkv, L, d, blk):
     assert_close_attn(got.numpy(), ref, f"{mode} B={B} L={L} d={d} b={blk}")
 
 
+# Scores that grow along the walk: a key component along one direction u
+# rises by RATE (natural-log units of score) per 64 keys of its position, and
+# every query carries A along u.  A later subtile's weights then exceed the
+# running maximum's by e^4 or more, so the online softmax moves its maximum
+# and rescales O on nearly every subtile (inside the fast loop, in boundary
+# tiles, across items), the two key-half groups of the split walk merge
+# different maxima, and key splits combine partials whose maxima differ by
+# hundreds.  Normal inputs reach that path only on a walk's first subtile.
+GROWING = [
+    # mode, B, Hq, Hkv, L, d, block
+    ("hybrid", 1, 8, 2, 512, 128, 32),       # one item per workgroup
+    ("hybrid", 2, 32, 8, 1024, 128, 32),     # 512 items: two per workgroup
+    ("hybrid", 1, 6, 2, 257, 64, 16),        # d = 64, ragged
+    ("decode", 2, 32, 8, 2000, 128, 28),     # split walk, group merge
+    ("causal", 1, 4, 1, 2048, 128, 128),     # persistent walk with key splits, then the combine
+    ("causal", 2, 8, 2, 700, 128, 700),      # prefill form
+]
+RATE, A = 8.0, 8.0
+
+
+@pytest.mark.parametrize("mode,B,Hq,Hkv,L,d,blk", GROWING)
+def test_growing_scores_elementwise(mode, B, Hq, Hkv, L, d, blk):
+    say(f"[attn growing scores] {mode} B={B} Hq={Hq} Hkv={Hkv} L={L} d={d} block={blk}")
+    q, k, v = _case(mode, B, Hq, Hkv, L, d, blk, seed=3000 + L + d + blk)
+    g = torch.Generator().manual_seed(L + d)
+    u = torch.randn(d, generator=g)
+    u = u / u.norm()
+    pos = torch.arange(k.shape[2], dtype=torch.float32)
+    if mode == "hybrid":
+        pos = pos % L                         # both halves grow along the position
+    c = RATE * pos / 64.0 * (d ** 0.5) / A
+    q = (q.float() + A * u).to(torch.bfloat16)
+    k = (k.float() + c[:, None] * u).to(torch.bfloat16)
+    got = _run(mode, q, k, v, blk)
+    ref = oracle.attention(mode, q, k, v, L, blk)
+    assert_close_attn(got.numpy(), ref, f"growing scores {mode} B={B} L={L} d={d} b={blk}")
+
+
 def _dense(case, what):
     """Every output element of a full-size workload against the oracle, in
     the launch configuration the benchmark times."""
