@@ -81,6 +81,34 @@ def test_bwd_elementwise(B, Hq, Hkv, L, d, blk):
     _check(dv, rv, ev, what + " dv")
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,L,d,blk", [(1, 8, 2, 300, 128, 32), (1, 4, 1, 130, 64, 7)])
+def test_bwd_growing_scores(B, Hq, Hkv, L, d, blk):
+    """Scores that rise by about 8 (natural-log units) per 64 keys of position
+    in both halves, so each row's weights sit on its last visible keys and
+    its log-sum-exp is far from 0: P is rebuilt from large scores minus a
+    large log-sum-exp."""
+    g = torch.Generator().manual_seed(4000 + L + d)
+    mk = lambda H: torch.randn(B, H, 2 * L, d, generator=g)
+    q, k, v, do = mk(Hq), mk(Hkv), mk(Hkv), mk(Hq)
+    u = torch.randn(d, generator=g)
+    u = u / u.norm()
+    c = 8.0 * (torch.arange(2 * L, dtype=torch.float32) % L) / 64.0 * (d ** 0.5) / 8.0
+    q, k = q + 8.0 * u, k + c[:, None] * u
+    q, k, v, do = (t.to(torch.bfloat16) for t in (q, k, v, do))
+    qd, kd, vd, dod = (t.to(dev()) for t in (q, k, v, do))
+    lse = torch.empty(B, Hq, 2 * L, dtype=torch.float32, device=dev())
+    out = bda.attn_fwd(qd, kd, vd, "hybrid", blk, lse=lse)
+    dq, dk, dv = bda.attn_bwd(qd, kd, vd, out, dod, lse, blk)
+    torch.cuda.synchronize()
+    rq, rk, rv, rl = oracle.attention_bwd("hybrid", q, k, v, do, L, blk)
+    eq, ek, ev = bwd_emul.grads(q, k, v, do, L, blk, o=out.cpu())
+    assert np.allclose(lse.cpu().numpy(), rl, rtol=0, atol=2e-3), "forward log-sum-exp"
+    what = f"growing scores B={B} Hq={Hq} L={L} d={d} b={blk}"
+    _check(dq, rq, eq, what + " dq")
+    _check(dk, rk, ek, what + " dk")
+    _check(dv, rv, ev, what + " dv")
+
+
 def test_bwd_rejects_other_modes():
     q = torch.zeros(1, 2, 8, 32, dtype=torch.bfloat16, device=dev())
     k = torch.zeros(1, 1, 16, 32, dtype=torch.bfloat16, device=dev())
