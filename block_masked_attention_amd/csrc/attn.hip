@@ -565,7 +565,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
           const int r = k * RPI + lane / CPR, c = lane % CPR;
           const u32x4 x = *(const u32x4*)(oreg + r * (2 * D) + ((c ^ (r & (CPR - 1))) << 4));
           const long long rr = __shfl(rowi, r);
-          if (rr >= 0) *(u32x4*)(a.out + (size_t)rr * D + 8 * c) = x;
+          // non-temporal: O is written once and not read here, and kept out
+          // of L2 it leaves room there for the K/V tiles of this XCD's
+          // (batch, kv head) pairs, which every later item re-reads
+          if (rr >= 0) __builtin_nontemporal_store(x, (u32x4*)(a.out + (size_t)rr * D + 8 * c));
         }
         // every wavefront has read its O back before the next item's first
         // tile copy goes into the ring stage
