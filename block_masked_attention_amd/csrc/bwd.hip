@@ -14,7 +14,8 @@
 //          transpose read, dS^T straight from the accumulator registers).
 //   dkdv   key-stationary: a workgroup keeps 128 keys of one (batch, kv
 //          head) in LDS and streams the blocks of 32 query slots (rows x
-//          heads of the group) that see them; two groups of 4 wavefronts (32
+//          heads of the group) that see them, from the end of the sequence
+//          down; two groups of 4 wavefronts (32
 //          keys each) take alternate blocks: S = Q K^T, dP = dO V^T
 //          (lane = key), dV += P^T dO and dK += dS^T Q (dO and Q by the LDS
 //          transpose read); the groups' partial dK, dV add at the end.
@@ -443,14 +444,28 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
 
   constexpr int QRUNS = QCH / 64;                         // 64-chunk runs of a Q block
   constexpr int QJ = (QRUNS + 3) / 4;                     // runs per wavefront of a group per matrix
+  // Blocks are taken from the end of the sequence down, the two ranges
+  // interleaved (both end at the same position for a clean tile), so the
+  // workgroups of one (batch, kv head) that run together read the same Q and
+  // dO rows at about the same time and share them in L2.
   auto block_row0 = [&](int t, int& half, int& r0, int& r1) {
-    if (t < na) {
+    const int m = imin(na, nb);
+    bool in_a;
+    int kb;
+    if (t < 2 * m) {
+      in_a = (t & 1) == 0;
+      kb = (in_a ? na : nb) - 1 - (t >> 1);
+    } else {
+      in_a = na > nb;
+      kb = (in_a ? na : nb) - 1 - (t - m);
+    }
+    if (in_a) {
       half = ha;
-      r0 = ra0 + t * rpb;
+      r0 = ra0 + kb * rpb;
       r1 = ra1;
     } else {
       half = 0;
-      r0 = rb0 + (t - na) * rpb;
+      r0 = rb0 + kb * rpb;
       r1 = rb1;
     }
   };
