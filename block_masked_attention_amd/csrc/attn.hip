@@ -511,6 +511,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
   // XOR-swizzled by the row, read back 16 bytes per lane so that each store
   // writes whole rows (D / 8 lanes per row) instead of 16 bytes of 32 rows.
   char* oreg = nullptr;
+  // finish() writes the 32-column tiles [fin_lo, fin_hi) of O and, if
+  // fin_rows, the per-row statistics (log-sum-exp, split max and sum): the
+  // split-key walk's two wavefront groups each write half of every row.
+  int fin_lo = 0, fin_hi = DT;
+  bool fin_rows = true;
   auto finish = [&]() {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
@@ -518,11 +523,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       if (!valid[qb]) continue;
       if (a.n_splits == 1) {
         const float inv = 1.f / l_tot;
-        if (LSE && hb == 0)
+        if (LSE && fin_rows && hb == 0)
           a.lse[attn_q_row(a, b, head[qb], qrow[qb])] = (m_run[qb] * sl2 + __log2f(l_tot)) * 0.6931471805599453f;
         uint16_t* op = a.out + attn_q_elem<D>(a, b, head[qb], qrow[qb]) + 4 * hb;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
+          if (dt < fin_lo || dt >= fin_hi) continue;
 #pragma unroll
           for (int i4 = 0; i4 < 4; ++i4) {
             u32x2 pk;
@@ -541,13 +547,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
         float* po = a.part_o + attn_part_elem<D>(a, cur.split, b, head[qb], qrow[qb]) + 4 * hb;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
+          if (dt < fin_lo || dt >= fin_hi) continue;
 #pragma unroll
           for (int i4 = 0; i4 < 4; ++i4) {
             f32x4 x{o[qb][dt][4 * i4], o[qb][dt][4 * i4 + 1], o[qb][dt][4 * i4 + 2], o[qb][dt][4 * i4 + 3]};
             *(f32x4*)(po + 32 * dt + 8 * i4) = x;
           }
         }
-        if (hb == 0) {
+        if (fin_rows && hb == 0) {
           float* pm = a.part_ml + prow * 2;
           pm[0] = m_run[qb] == -INFINITY ? -INFINITY : m_run[qb] * sl2;
           pm[1] = l_tot;
@@ -666,36 +673,59 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       settle_for(i + 1, issued);
     }
     drain();
-    // group 1 hands its state to group 0 through the (drained) ring
+    // The two groups hold (max, sum, O) of the same slots over different
+    // keys.  Each hands the other the 32-column tiles of O that the other
+    // keeps, with its max and sum, through the (drained) ring; each then
+    // merges and writes half of every row (group kg: tiles [kg DT/2, (kg+1)
+    // DT/2)).  Both form the row's max and sum from the same two operands,
+    // so both normalise by the same value.  D = 32 (one tile): group 1 hands
+    // everything to group 0.
     float* xf = reinterpret_cast<float*>(smem);
-    constexpr int NE = DT * 16 + 2;
-    auto xi = [&](int qb, int e) { return ((wq * NQB + qb) * NE + e) * 64 + lane; };
-    static_assert(NWQ * NQB * NE * 64 * 4 <= STAGES * STAGE * 2, "merge buffer exceeds the ring");
-    if (kg == 1) {
+    constexpr int HD = DT >= 2 ? DT / 2 : DT;      // tiles a group keeps
+    constexpr int NE = HD * 16 + 2;
+    auto xi = [&](int g, int qb, int e) { return (((g * NWQ + wq) * NQB + qb) * NE + e) * 64 + lane; };
+    static_assert(2 * NWQ * NQB * NE * 64 * 4 <= STAGES * STAGE * 2, "merge buffer exceeds the ring");
+    // Tiles [t0, t0 + HD) of O go out (wave-uniform branches keep every
+    // register index a constant).
+    auto give_tiles = [&](int qb, int t0) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < HD; ++j)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xf[xi(kg, qb, j * 16 + i)] = o[qb][t0 + j][i];
+    };
+    if (DT >= 2 || kg == 1) {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) xf[xi(qb, dt * 16 + i)] = o[qb][dt][i];
-        xf[xi(qb, DT * 16)] = m_run[qb];
-        xf[xi(qb, DT * 16 + 1)] = l_run[qb];
+        if (DT < 2 || kg == 1) give_tiles(qb, 0);
+        else give_tiles(qb, DT - HD);
+        xf[xi(kg, qb, HD * 16)] = m_run[qb];
+        xf[xi(kg, qb, HD * 16 + 1)] = l_run[qb];
       }
     }
     __syncthreads();
-    if (kg == 0) {
+    if (DT >= 2 || kg == 0) {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
-        const float mb = xf[xi(qb, DT * 16)], lb = xf[xi(qb, DT * 16 + 1)];
+        const int other = 1 - kg;
+        const float mb = xf[xi(other, qb, HD * 16)], lb = xf[xi(other, qb, HD * 16 + 1)];
         const float M = fmaxf(m_run[qb], mb);
         const float fa = m_run[qb] == -INFINITY ? 0.f : exp2_fast((m_run[qb] - M) * sl2);
         const float fb = mb == -INFINITY ? 0.f : exp2_fast((mb - M) * sl2);
         l_run[qb] = l_run[qb] * fa + lb * fb;
         m_run[qb] = M;
+        auto take_tiles = [&](int t0) __attribute__((always_inline)) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+          for (int j = 0; j < HD; ++j)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) o[qb][dt][i] = o[qb][dt][i] * fa + xf[xi(qb, dt * 16 + i)] * fb;
+            for (int i = 0; i < 16; ++i) o[qb][t0 + j][i] = o[qb][t0 + j][i] * fa + xf[xi(other, qb, j * 16 + i)] * fb;
+        };
+        if (kg == 0) take_tiles(0);
+        else take_tiles(DT - HD);
+      }
+      if constexpr (DT >= 2) {
+        fin_lo = kg * HD;
+        fin_hi = fin_lo + HD;
+        fin_rows = kg == 0;
       }
       finish();
     }
