@@ -99,9 +99,22 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
   int qrow[NQB], head[NQB];
   bool valid[NQB];
   bf16x8 qreg[NQB][KSTEPS];
+  // The Q operands of the current item's slots (lane (ql, hb) holds d =
+  // 16*ks + 8*hb + 0..7); the compiler places the wait for them.
+  auto load_q = [&]() {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const uint16_t* qp = a.q + attn_q_elem<D>(a, b, head[qb], qrow[qb]) + 8 * hb;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        u32x4 x = valid[qb] ? *(const u32x4*)(qp + 16 * ks) : u32x4{0, 0, 0, 0};
+        qreg[qb][ks] = __builtin_bit_cast(bf16x8, x);
+      }
+    }
+  };
   // Switch to item idx: its geometry, my query slots (one per column block)
-  // and their Q operands (lane (ql, hb) holds d = 16*ks + 8*hb + 0..7).
-  auto begin_item = [&](int idx) {
+  // and, with with_q, their Q operands.
+  auto begin_item = [&](int idx, bool with_q = true) {
     geom(idx, cur);
     b = cur.pair / a.Hkv;
     g = cur.pair - b * a.Hkv;
@@ -117,12 +130,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       } else {
         valid[qb] = attn_slot(a, 0, (wq * NQB + qb) * 32 + ql, cur.qt, g, qrow[qb], head[qb]);
       }
-      const uint16_t* qp = a.q + attn_q_elem<D>(a, b, head[qb], qrow[qb]) + 8 * hb;
+    }
+    if (with_q) load_q();
+  };
+  // The Q operands of the current item's slots, loaded and waited for in
+  // one statement (the wait also covers every load issued before it).  A
+  // slot without a row reads the first row of Q and keeps zeros.
+  auto load_q_wait = [&]() {
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        u32x4 x = valid[qb] ? *(const u32x4*)(qp + 16 * ks) : u32x4{0, 0, 0, 0};
-        qreg[qb][ks] = __builtin_bit_cast(bf16x8, x);
-      }
+    for (int qb = 0; qb < NQB; ++qb) {
+      const uint16_t* qp = a.q + (valid[qb] ? attn_q_elem<D>(a, b, head[qb], qrow[qb]) + 8 * hb : 0);
+      u32x4 x[KSTEPS];
+      load_x16_stride32_wait<KSTEPS>(qp, x);
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks)
+        qreg[qb][ks] = __builtin_bit_cast(bf16x8, valid[qb] ? x[ks] : u32x4{0, 0, 0, 0});
     }
   };
 
@@ -630,7 +652,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
     // up to four 64-key tiles in flight; wavefront group kg computes the
     // 32-key half kg of every tile for all the item's query slots, and the
     // two groups merge their (max, sum, O) through LDS at the end.
-    begin_item(blockIdx.x);
+    begin_item(blockIdx.x, false);
     reset_acc();
     const int nf = cur.nf, nt = cur.nt;
     auto stq = [&](int j) { return j % STAGES; };
@@ -651,9 +673,28 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(const AttnArgs a) 
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     };
+    // A short walk (a key split of a few tiles) sends tile 0's copy first
+    // and the Q operands after it, in a statement that waits for both; tiles
+    // 1 .. 3 follow, so tile 0's arithmetic starts while they load.  (Q
+    // loaded the ordinary way would be waited for at its first use, and the
+    // compiler, which does not count the copies, would wait there for every
+    // load: vmcnt(0).)  A long walk keeps four tiles in flight from the start
+    // and waits for all of them with Q: the stream, not the first tile's
+    // arithmetic, is what bounds it.
     int issued = 0;
-    for (; issued < STAGES - 1 && issued < nt; ++issued) dma(cur, issued, stq(issued));
-    drain();   // the Q operands and the first tiles
+    if (nt <= 8) {
+      if (nt > 0) dma(cur, 0, stq(0)), issued = 1;
+      load_q_wait();
+      for (; issued < STAGES - 1 && issued < nt; ++issued) dma(cur, issued, stq(issued));
+      // every wavefront's share of tile 0 has landed
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    } else {
+      load_q();
+      for (; issued < STAGES - 1 && issued < nt; ++issued) dma(cur, issued, stq(issued));
+      drain();   // the Q operands and the first tiles
+    }
     // Tile i + 4 goes into the stage of tile i - 1, which every wavefront
     // finished before the last barrier.
 #pragma unroll 1

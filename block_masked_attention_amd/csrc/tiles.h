@@ -88,6 +88,49 @@ __device__ __forceinline__ void lds_dma16_sa_nt(const void* base, unsigned off, 
 
 #pragma clang diagnostic pop
 
+// N 16-byte loads at p + 32 k bytes (k = 0 .. N-1) into x[k], followed in the
+// same statement by a wait for every vector-memory load of the wavefront
+// issued up to that point (these and any issued before them), so the
+// outputs are written when the statement ends.
+template <int N>
+__device__ __forceinline__ void load_x16_stride32_wait(const void* p, u32x4 (&x)[N]) {
+  static_assert(N == 2 || N == 4 || N == 8, "2, 4 or 8 loads");
+  if constexpr (N == 8) {
+    asm volatile(
+        "global_load_dwordx4 %0, %8, off\n\t"
+        "global_load_dwordx4 %1, %8, off offset:32\n\t"
+        "global_load_dwordx4 %2, %8, off offset:64\n\t"
+        "global_load_dwordx4 %3, %8, off offset:96\n\t"
+        "global_load_dwordx4 %4, %8, off offset:128\n\t"
+        "global_load_dwordx4 %5, %8, off offset:160\n\t"
+        "global_load_dwordx4 %6, %8, off offset:192\n\t"
+        "global_load_dwordx4 %7, %8, off offset:224\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]),
+          "=&v"(x[7])
+        : "v"(p)
+        : "memory");
+  } else if constexpr (N == 4) {
+    asm volatile(
+        "global_load_dwordx4 %0, %4, off\n\t"
+        "global_load_dwordx4 %1, %4, off offset:32\n\t"
+        "global_load_dwordx4 %2, %4, off offset:64\n\t"
+        "global_load_dwordx4 %3, %4, off offset:96\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+        : "v"(p)
+        : "memory");
+  } else {
+    asm volatile(
+        "global_load_dwordx4 %0, %2, off\n\t"
+        "global_load_dwordx4 %1, %2, off offset:32\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1])
+        : "v"(p)
+        : "memory");
+  }
+}
+
 // ds_read_b64_tr_b16: within each 16-lane group, lane j receives element
 // (j & 3) of the 4-element row read by lane 4*e + (j >> 2), for e = 0..3.
 __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
