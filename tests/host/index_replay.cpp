@@ -146,7 +146,9 @@ static void ring_replay(const AttnIndex& a, const int32_t* kv_len, long long gri
 }
 
 // The split-key walk's DMA ring as attn.hip runs it, for one item: tile t
-// goes to stage t % 5; the prologue issues up to four and waits for all.
+// goes to stage t % 5.  The prologue of a long walk (more than 8 tiles)
+// issues up to four and waits for all; that of a short walk issues tile 0,
+// waits for it (the statement that loads Q), then issues tiles 1 .. 3.
 // Step i first issues the next tile (into the stage of tile i - 1, which the
 // step before finished), reads tile i, then waits until tile i + 1 has
 // landed (up to three tiles issued after it stay in flight) and the
@@ -165,8 +167,14 @@ static void split_ring_replay(const Geom& gm, const char* what, int idx) {
     CHECK(ok, "%s: split item %d reads tile %lld of %d before it landed or after its stage was reused", what, idx,
           t, nt);
   };
-  for (int k = 0; k < 4; ++k) issue();
-  landed = issued;
+  if (nt <= 8) {
+    issue();
+    landed = issued;
+    for (int k = 1; k < 4; ++k) issue();
+  } else {
+    for (int k = 0; k < 4; ++k) issue();
+    landed = issued;
+  }
   for (int i = 0; i < nt; ++i) {
     issue();
     read(i);
