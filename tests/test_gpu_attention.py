@@ -58,6 +58,11 @@ SMALL = [
     ("causal", 1, 8, 2, 256, 128, 129),    # last query tile (one row) sees all 256 keys
     ("decode", 1, 4, 1, 20, 128, 20),      # fewer keys than half a tile: one key group sees none
     ("causal", 1, 4, 1, 2048, 128, 128),   # persistent walk with 8 key splits (partials, then the combine)
+    # split-key walk prologues: walks of at most 8 tiles start on tile 0 while
+    # tiles 1..3 load, longer walks wait for four tiles first
+    ("decode", 4, 32, 8, 4096, 128, 28),   # 8 splits of exactly 8 tiles (the short prologue's largest walk)
+    ("decode", 4, 32, 8, 4608, 128, 28),   # 8 splits of 9 tiles (the long prologue's smallest walk)
+    ("causal", 4, 32, 8, 4100, 128, 28),   # 7 splits of 9 tiles and a ragged last split of 2 tiles: both in one launch
 ]
 
 
