@@ -63,9 +63,9 @@ SMALL = [
     ("decode", 4, 32, 8, 4096, 128, 28),   # 8 splits of exactly 8 tiles (the short prologue's largest walk)
     ("decode", 4, 32, 8, 4608, 128, 28),   # 8 splits of 9 tiles (the long prologue's smallest walk)
     ("causal", 4, 32, 8, 4100, 128, 28),   # 7 splits of 9 tiles and a ragged last split of 2 tiles: both in one launch
-    # persistent training-form walk at d = 32 and 64: items whose rows lie in
-    # one block and whose clean prefix ends on a 64-key boundary stage their
-    # own clean block and own noisy block in one mixed tile
+    # persistent training-form walk at d = 32 and 64 (one 8-wave workgroup per
+    # CU for d = 128, two below), items of one block's rows with 32-key
+    # boundary ranges
     ("hybrid", 1, 4, 1, 512, 32, 16),
     ("hybrid", 2, 8, 2, 640, 64, 32),
 ]
